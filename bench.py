@@ -1,0 +1,362 @@
+"""Benchmark of the batch-invariant forward reductions on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-twins]
+
+A *step* is one pass of the whole hot path over one batch of synthetic
+Qwen3-235B-A22B-shaped input, every kernel batch-invariant:
+    rmsnorm_bi   x [8192, 4096] bf16 (1% of rows x100), eps 1e-6
+    matmul_bi    QKV   [4096, 4096] . [9216, 4096]^T  (bf16 in, fp32 acc, bf16 out)
+    matmul_bi    o_proj[4096, 8192] . [4096, 8192]^T
+    kv_append    one new token per request (256 x 4 kv heads x 128)
+    decode_attn_bi  batch 256, 64 query / 4 kv heads, head_dim 128, page 16,
+                 split 256, KV lengths ~ U{1..32768}
+Inputs are resident in HBM before the timed region; RMSNorm and matmul operands
+rotate over 4 buffer sets (> 512 MB) so the 256 MB last-level cache does not
+serve them warm.  ``value`` = algorithmic HBM bytes of the step / step time.
+
+Printed: ONE JSON line with the metric, a per-kernel breakdown (HBM GB/s or MFMA
+TFLOP/s against the chip's peak), the ``roofline`` object of the dominant kernel
+(decode attention), the shape-tuned twins' times and the determinism slowdown
+(t_bi / t_tuned - 1), and the CPU oracle timed on a bounded sample of the same
+workload (``cpu_baseline``).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import subprocess
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import invariant_rmsnorm_bi_amd as rbi  # noqa: E402
+import synth  # noqa: E402
+
+METRIC = "HBM GB/s & MFMA TFLOP/s of batch-invariant kernels; % slowdown vs tuned twins"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+DEV = "cuda"
+
+H = 4096
+RMS_ROWS = 8192
+MM_M = 4096
+QKV = (9216, 4096)
+OPROJ = (4096, 8192)
+ATT_B, HQ, HKV, D, PAGE, SPLIT, LMAX = 256, 64, 4, 128, 16, 256, 32768
+SETS = 4
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------------------
+# algorithmic work per call (the method's own bytes / flops, no implementation overhead)
+# --------------------------------------------------------------------------------------
+
+def rms_bytes(rows, hidden=H):
+    return rows * hidden * 2 * 2 + hidden * 2
+
+
+def mm_bytes(M, N, K):
+    return 2 * (M * K + N * K + M * N)
+
+
+def mm_flops(M, N, K):
+    return 2 * M * N * K
+
+
+def attn_bytes(lens):
+    # K and V of every cached token and kv head, q in, out
+    return int(sum(lens)) * HKV * D * 2 * 2 + len(lens) * HQ * D * 2 * 2
+
+
+def append_bytes(tokens):
+    return tokens * HKV * D * 2 * 2 * 2
+
+
+# --------------------------------------------------------------------------------------
+# workload
+# --------------------------------------------------------------------------------------
+
+class Workload:
+    def __init__(self):
+        t0 = time.time()
+        self.x = [synth.rmsnorm_rows(RMS_ROWS, H, seed=synth.SEED_DATA + i, device=DEV)
+                  for i in range(SETS)]
+        self.y = [torch.empty_like(self.x[0]) for _ in range(SETS)]
+        self.w_ln = synth.normal((H,), std=0.1, mean=1.0, seed=synth.SEED_WEIGHTS, device=DEV)
+        self.a_qkv = [synth.normal((MM_M, QKV[1]), seed=10 + i, device=DEV) for i in range(SETS)]
+        self.w_qkv = [synth.normal(QKV, std=0.02, seed=20 + i, device=DEV) for i in range(SETS)]
+        self.a_o = [synth.normal((MM_M, OPROJ[1]), seed=30 + i, device=DEV) for i in range(SETS)]
+        self.w_o = [synth.normal(OPROJ, std=0.02, seed=40 + i, device=DEV) for i in range(SETS)]
+        self.c_qkv = torch.empty((MM_M, QKV[0]), dtype=torch.bfloat16, device=DEV)
+        self.c_o = torch.empty((MM_M, OPROJ[0]), dtype=torch.bfloat16, device=DEV)
+        # paged decode attention: lengths include this step's new token
+        self.lens = synth.uniform_lengths(ATT_B, 1, LMAX, seed=synth.SEED_BATCH)
+        self.kv = synth.paged_kv(self.lens, HKV, D, PAGE, max_pages=LMAX // PAGE, device=DEV)
+        self.q = synth.normal((ATT_B, HQ, D), seed=50, device=DEV)
+        self.k_new = synth.normal((ATT_B, HKV, D), seed=51, device=DEV)
+        self.v_new = synth.normal((ATT_B, HKV, D), seed=52, device=DEV)
+        bt = self.kv.block_table.cpu()
+        slots = [int(bt[r, (L - 1) // PAGE]) * PAGE + (L - 1) % PAGE
+                 for r, L in enumerate(self.lens)]
+        self.slots = torch.tensor(slots, dtype=torch.int32, device=DEV)
+        self.att_out = torch.empty((ATT_B, HQ, D), dtype=torch.bfloat16, device=DEV)
+        self.ws = torch.empty(rbi.decode_attn_workspace_size(ATT_B, HQ, D, LMAX, SPLIT),
+                              dtype=torch.uint8, device=DEV)
+        torch.cuda.synchronize()
+        log(f"workload ready in {time.time() - t0:.1f}s: KV tokens {sum(self.lens)}, "
+            f"cache {self.kv.k_cache.numel() * 4 / 1e9:.2f} GB")
+
+    # the kernels of one step, by name, each a closure over buffer set i
+    def calls(self, i):
+        s = i % SETS
+        return [
+            ("rmsnorm_bi", lambda: rbi.rmsnorm_bi(self.x[s], self.w_ln, 1e-6, out=self.y[s])),
+            ("matmul_bi_qkv", lambda: rbi.matmul_bi(self.a_qkv[s], self.w_qkv[s], out=self.c_qkv)),
+            ("matmul_bi_oproj", lambda: rbi.matmul_bi(self.a_o[s], self.w_o[s], out=self.c_o)),
+            ("kv_append", lambda: rbi.kv_append(self.k_new, self.v_new, self.slots,
+                                                self.kv.k_cache, self.kv.v_cache)),
+            ("decode_attn_bi", lambda: rbi.decode_attn_bi(
+                self.q, self.kv.k_cache, self.kv.v_cache, self.kv.block_table, self.kv.kv_lens,
+                LMAX, SPLIT, out=self.att_out, workspace=self.ws)),
+        ]
+
+    def work(self):
+        return {
+            "rmsnorm_bi": dict(bytes=rms_bytes(RMS_ROWS), bound="hbm"),
+            "matmul_bi_qkv": dict(bytes=mm_bytes(MM_M, *QKV), flops=mm_flops(MM_M, *QKV),
+                                  bound="mfma"),
+            "matmul_bi_oproj": dict(bytes=mm_bytes(MM_M, *OPROJ), flops=mm_flops(MM_M, *OPROJ),
+                                    bound="mfma"),
+            "kv_append": dict(bytes=append_bytes(ATT_B), bound="hbm"),
+            "decode_attn_bi": dict(bytes=attn_bytes(self.lens), bound="hbm"),
+        }
+
+
+# --------------------------------------------------------------------------------------
+# timing helpers
+# --------------------------------------------------------------------------------------
+
+def time_fn(fn, reps=20, warm=3):
+    """Median device time (ms) of fn over reps, hipEvents on the current stream."""
+    for _ in range(warm):
+        fn()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts))
+
+
+def twin_points(wl: Workload):
+    """(name, bi_fn, tuned_fn) at the slowdown points: RMSNorm batch sizes, matmul M
+    for both projections, attention batch sizes."""
+    pts = []
+    for B in (1, 64, 512, 4096, 8192):
+        x = wl.x[0][:B]
+        y = wl.y[0][:B]
+        pts.append((f"rmsnorm B={B}",
+                    lambda x=x, y=y: rbi.rmsnorm_bi(x, wl.w_ln, 1e-6, out=y),
+                    lambda x=x, y=y: rbi.rmsnorm_tuned(x, wl.w_ln, 1e-6, out=y)))
+    for nm, A, W, C, K in (("qkv", wl.a_qkv[0], wl.w_qkv[0], wl.c_qkv, QKV[1]),
+                           ("oproj", wl.a_o[0], wl.w_o[0], wl.c_o, OPROJ[1])):
+        for M in (1, 7, 64, 127, 256, 509, 1024, 2039, 4096):
+            ws = torch.empty(max(16, rbi.matmul_tuned_workspace_size(M, W.shape[0], K)),
+                             dtype=torch.uint8, device=DEV)
+            pts.append((f"matmul {nm} M={M}",
+                        lambda A=A[:M], W=W, C=C[:M]: rbi.matmul_bi(A, W, out=C),
+                        lambda A=A[:M], W=W, C=C[:M], ws=ws: rbi.matmul_tuned(A, W, out=C,
+                                                                              workspace=ws)))
+    kv = wl.kv
+    for B in (1, 16, 64, 256):
+        bt, ln, q = kv.block_table[:B], kv.kv_lens[:B], wl.q[:B]
+        out = wl.att_out[:B]
+        host = wl.lens[:B]
+        split_t = rbi.decode_attn_tuned_split_size(B, HKV, LMAX, host)
+        ws_t = torch.empty(rbi.decode_attn_workspace_size(B, HQ, D, LMAX, split_t),
+                           dtype=torch.uint8, device=DEV)
+        pts.append((f"decode_attn batch={B}",
+                    lambda bt=bt, ln=ln, q=q, out=out: rbi.decode_attn_bi(
+                        q, kv.k_cache, kv.v_cache, bt, ln, LMAX, SPLIT, out=out, workspace=wl.ws),
+                    lambda bt=bt, ln=ln, q=q, out=out, host=host, ws_t=ws_t: rbi.decode_attn_tuned(
+                        q, kv.k_cache, kv.v_cache, bt, ln, LMAX, kv_lens_host=host, out=out,
+                        workspace=ws_t)))
+    return pts
+
+
+# --------------------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample of the same workload)
+# --------------------------------------------------------------------------------------
+
+def cpu_baseline(wl: Workload, step_bytes: float):
+    import oracle
+    t_start = time.time()
+    samples = {}
+    # RMSNorm: 512 of the 8192 rows
+    xs = synth.bf16_bits(wl.x[0][:512])
+    wln = synth.bf16_bits(wl.w_ln)
+    t = time.perf_counter()
+    oracle.rmsnorm(xs, wln, 1e-6)
+    samples["rmsnorm"] = (time.perf_counter() - t) * (RMS_ROWS / 512)
+    # matmul: rows of A against the full weight (the oracle's cost is linear in M)
+    for nm, A, W in (("qkv", wl.a_qkv[0], wl.w_qkv[0]), ("oproj", wl.a_o[0], wl.w_o[0])):
+        m = 16
+        a, w = synth.bf16_bits(A[:m]), synth.bf16_bits(W)
+        t = time.perf_counter()
+        oracle.matmul(a, w)
+        samples["matmul_" + nm] = (time.perf_counter() - t) * (MM_M / m)
+    # attention: 8 requests (cost linear in their total length)
+    rows = list(range(8))
+    kc, vc = synth.bf16_bits(wl.kv.k_cache), synth.bf16_bits(wl.kv.v_cache)
+    bt = wl.kv.block_table.cpu().numpy()[rows]
+    lens = np.array([wl.lens[r] for r in rows], dtype=np.int32)
+    q = synth.bf16_bits(wl.q[rows])
+    t = time.perf_counter()
+    oracle.decode_attn(q, kc, vc, bt, lens, 1 / math.sqrt(D))
+    samples["decode_attn"] = (time.perf_counter() - t) * (sum(wl.lens) / lens.sum())
+    t_step = sum(samples.values())
+    return {
+        "value": round(step_bytes / t_step / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": ("fp64 C oracle (OpenMP) on 512 of 8192 RMSNorm rows, 16 of 4096 rows of "
+                   "each projection, 8 of 256 attention requests "
+                   f"({int(lens.sum())} KV tokens); each scaled linearly to the full step"),
+        "seconds_per_step_extrapolated": round(t_step, 2),
+        "sample_wall_s": round(time.time() - t_start, 1),
+    }
+
+
+def fingerprint():
+    p = torch.cuda.get_device_properties(0)
+    try:
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short", "HEAD"],
+                             capture_output=True, text=True).stdout.strip()
+    except Exception:
+        sha = ""
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"gpu": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
+            "torch": torch.__version__, "hip": torch.version.hip, "git": sha, "host_cpu": cpu,
+            "host_threads": os.cpu_count(), "python": platform.python_version(),
+            "seeds": {"data": synth.SEED_DATA, "weights": synth.SEED_WEIGHTS,
+                      "batch": synth.SEED_BATCH, "pages": synth.SEED_PAGES}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-twins", action="store_true", help="skip the tuned-twin comparison")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(kernels are per-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    rbi.lib()
+    wl = Workload()
+
+    # warmup
+    for i in range(args.warmup):
+        for _, fn in wl.calls(i):
+            fn()
+    torch.cuda.synchronize()
+
+    # timed region: K steps; hipEvents around every kernel call, on the launch stream
+    names = [n for n, _ in wl.calls(0)]
+    ev = {n: [] for n in names}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for n, fn in wl.calls(i):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ev[n].append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    work = wl.work()
+    kernels = {}
+    for n in names:
+        us = float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) * 1e3
+        w = work[n]
+        k = {"us": round(us, 2), "bytes": w["bytes"],
+             "GB/s": round(w["bytes"] / us / 1e3, 1)}
+        if w["bound"] == "mfma":
+            tf = w["flops"] / us / 1e6
+            k.update({"flops": w["flops"], "TFLOP/s": round(tf, 1),
+                      "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFS, 4)})
+        else:
+            k["frac_hbm_peak"] = round(w["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4)
+        kernels[n] = k
+    step_bytes = sum(w["bytes"] for w in work.values())
+    value = step_bytes / (ms_step / 1e3) / 1e9
+
+    dom = kernels["decode_attn_bi"]
+    roofline = {"bound": "hbm", "kernel": "decode_attn_bi (split + ordered merge)",
+                "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": dom["bytes"], "avg_launch_us": dom["us"]}
+
+    twins = None
+    if not args.no_twins:
+        log("timing the tuned twins")
+        pts = []
+        for name, fbi, ftu in twin_points(wl):
+            tb, tt = time_fn(fbi), time_fn(ftu)
+            pts.append({"point": name, "bi_us": round(tb * 1e3, 2), "tuned_us": round(tt * 1e3, 2),
+                        "slowdown_pct": round((tb / tt - 1) * 100, 2)})
+        mean = float(np.mean([p["slowdown_pct"] for p in pts]))
+        twins = {"points": pts, "mean_slowdown_pct": round(mean, 2),
+                 "unit": "time increase of bi over tuned, percent"}
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(wl, step_bytes)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": ("qwen3-235b-a22b-shaped batch-invariant step: rmsnorm_bi "
+                                "[8192,4096] + matmul_bi QKV [4096,4096]x[9216,4096]^T + o_proj "
+                                "[4096,8192]x[4096,8192]^T + kv_append + decode_attn_bi batch 256 "
+                                "(64q/4kv heads, d128, page 16, split 256, L~U{1..32768})"),
+                   "step_bytes": step_bytes, "buffer_sets": SETS},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "twins": twins,
+        "fingerprint": fingerprint(),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,236 @@
+/*
+ * rbi.h -- C ABI of the batch-invariant forward-reduction library for AMD
+ * MI355X (gfx950): librbi.so.
+ *
+ * Property delivered by every *_bi entry point ("batch invariance"): the bits
+ * of each output row depend only on that row's own inputs (and, for attention,
+ * on its own KV length and cache contents), never on how many other rows are in
+ * the call, where the row sits in the batch, what its neighbours hold, or how a
+ * sequence was cut into prefill chunks.  Sources (web pages, by title/section):
+ *   [P1] "Reproducible LLM Inference - Batch Invariance, the Cost of
+ *        Determinism, and Where Bitwise Identity Is Actually Required"
+ *        (hidekazu-konishi.com), sections 5.1-5.5.
+ *   [P3] "Your Answer Depends on Who Else Is in the Batch" (praveentn.live),
+ *        "Where the reductions are", "The attention detail that gets missed".
+ * Each *_tuned entry point is a deliberately shape-tuned twin that computes the
+ * same function but picks its reduction split from the shape, so it is
+ * run-to-run deterministic but NOT batch-invariant; it exists to price
+ * determinism.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or from a framework
+ *    allocator) unless an argument says "host".  The caller owns all memory.
+ *    The library never allocates, frees or synchronises, and keeps no mutable
+ *    global state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *    enqueued asynchronously on it; results are ready when the stream is.
+ *  - Return value: RBI_OK (0) or a negative status.  Arguments are validated
+ *    before anything is enqueued; on error nothing is enqueued and no memory is
+ *    touched.  A zero-sized problem (rows == 0, M == 0, tokens == 0) is a no-op
+ *    that returns RBI_OK.  No C++ exception crosses this boundary.
+ *  - Layouts are row-major; strides are in ELEMENTS.  bf16 is IEEE bfloat16
+ *    stored as 16-bit words; every rounding to bf16 is round-to-nearest-even.
+ *  - No kernel uses atomics: repeated calls on the same inputs give the same
+ *    bits (run-to-run determinism, [P1] sections 4.2-4.3).
+ */
+#ifndef RBI_H
+#define RBI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum { RBI_F32 = 0, RBI_BF16 = 1 };
+
+/* status codes */
+enum {
+    RBI_OK = 0,
+    RBI_EINVAL = -1,       /* null pointer, negative size, bad stride or alignment */
+    RBI_EUNSUPPORTED = -2, /* valid but outside what the kernels implement        */
+    RBI_EWORKSPACE = -3,   /* workspace pointer null or smaller than required      */
+    RBI_ELAUNCH = -4       /* the HIP runtime refused a kernel launch               */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *rbi_status_string(int status);
+
+/* Library ABI version, incremented on any signature change. */
+int rbi_abi_version(void);
+
+/* -------------------------------------------------------------------------- */
+/* RMSNorm                                                                     */
+/* -------------------------------------------------------------------------- */
+/*
+ * rmsnorm_bi: y[r,i] = x[r,i] * (1 / sqrt(sum_j x[r,j]^2 / hidden + eps)) * w[i]
+ * ([P1] section 5.4 "The Three Operations That Involve a Reduction", first
+ * operation; [P3] "A Concrete Example").  Each row is reduced by ONE wavefront
+ * in an order fixed by `hidden` alone ([P1] section 5.3: one row per core, so
+ * the order is the same at any batch size): lane-strided fp32 partial sums over
+ * 16-byte chunks, then a fixed xor-butterfly across the 64 lanes.  The scale and
+ * product are formed in fp32, (x * r) * w, and rounded once to the output type.
+ *
+ *  x      [rows, hidden], row stride x_row_stride; dtype RBI_F32 or RBI_BF16
+ *  w      [hidden], same dtype as x
+ *  y      [rows, hidden], row stride y_row_stride, same dtype; may alias x when
+ *         the strides are equal (each row is read fully before it is written)
+ *  eps    added to the mean of squares, inside the root
+ * Requirements: x, y, w 16-byte aligned; row strides multiples of 16 bytes
+ * (8 bf16 / 4 fp32 elements) and >= hidden; hidden >= 1.  Otherwise RBI_EINVAL.
+ */
+int rmsnorm_bi(const void *x, int64_t x_row_stride, const void *w, void *y,
+               int64_t y_row_stride, int64_t rows, int64_t hidden, float eps, int dtype,
+               void *stream);
+
+/*
+ * rmsnorm_tuned: same function and arguments.  When rows are too few to fill
+ * the chip it spreads each row over a whole 256-thread workgroup (a different
+ * reduction tree), otherwise it uses the one-wavefront-per-row layout; the bits
+ * of a row therefore depend on the batch size ([P1] section 5.3, the
+ * small-batch split that breaks invariance).
+ */
+int rmsnorm_tuned(const void *x, int64_t x_row_stride, const void *w, void *y,
+                  int64_t y_row_stride, int64_t rows, int64_t hidden, float eps, int dtype,
+                  void *stream);
+
+/* -------------------------------------------------------------------------- */
+/* Matmul                                                                      */
+/* -------------------------------------------------------------------------- */
+/*
+ * matmul_bi: C[m,n] = sum_k A[m,k] * W[n,k]   (C = A . W^T, W stored [N, K] as a
+ * linear layer's weight).  bf16 inputs, fp32 accumulation, one rounding to
+ * c_dtype (RBI_BF16 or RBI_F32).  [P1] section 5.4, second operation: one
+ * kernel configuration for every shape -- no split-K and no change of matrix
+ * instruction with M.  Every output element is accumulated by the same
+ * sequence of v_mfma_f32_16x16x32_bf16 steps over K in ascending 32-wide
+ * blocks, starting from zero, whatever M, N or its position in the tile.
+ *
+ *  A  [M, K] bf16, row stride lda;  W [N, K] bf16, row stride ldw;
+ *  C  [M, N] c_dtype, row stride ldc.
+ * Requirements: A, W 16-byte aligned, lda and ldw multiples of 8, K a positive
+ * multiple of 8, lda >= K, ldw >= K; C 16-byte aligned, ldc a multiple of 4,
+ * ldc >= N, N a multiple of 4.  Otherwise RBI_EINVAL.
+ */
+int matmul_bi(const void *A, int64_t lda, const void *W, int64_t ldw, void *C, int64_t ldc,
+              int c_dtype, int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * matmul_tuned: same function.  Chooses split-K from (M, N, K) so that small-M
+ * problems fill the chip; split partials are reduced in ascending split order by
+ * a second kernel (deterministic run to run, but the K partition -- and so the
+ * bits -- changes with M: [P1] section 5.4, "split reduction, also known as
+ * split-K").  Needs `workspace` of matmul_tuned_workspace_size(M, N, K) bytes
+ * (0 means none is needed; NULL is then allowed).
+ */
+size_t matmul_tuned_workspace_size(int64_t M, int64_t N, int64_t K);
+int matmul_tuned(const void *A, int64_t lda, const void *W, int64_t ldw, void *C, int64_t ldc,
+                 int c_dtype, int64_t M, int64_t N, int64_t K, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* -------------------------------------------------------------------------- */
+/* Paged split-KV decode attention                                             */
+/* -------------------------------------------------------------------------- */
+/*
+ * decode_attn_bi: one query token per row, grouped-query heads, over a paged
+ * KV cache, split along the KV length at a FIXED SPLIT SIZE ([P1] section 5.5
+ * "Why Attention Is the Hardest Case"; [P3] "The attention detail that gets
+ * missed").  For row r with length L = kv_lens[r] and query head h (kv head
+ * g = h / (num_q_heads / num_kv_heads)):
+ *     out[r,h] = sum_{j<L} softmax_j(scale * <q[r,h], k_j>) v_j
+ * where k_j, v_j sit in page block_table[r][j / page_size], slot
+ * j % page_size.  Split s covers tokens [s*split_size, min((s+1)*split_size, L));
+ * the boundaries depend on nothing but L.  Per split the kernel forms a partial
+ * (max m, sum l, accumulator acc) with bf16 MFMA products and fp32 softmax;
+ * a second kernel combines the ceil(L / split_size) partials in ascending split
+ * order (log-sum-exp rescaling) and rounds acc / l to bf16 once.
+ *
+ *  q            [rows, num_q_heads, head_dim] bf16, row stride q_row_stride
+ *               (head stride head_dim)
+ *  k_cache,
+ *  v_cache      [num_pages, num_kv_heads, page_size, head_dim] bf16
+ *  block_table  [rows, bt_stride] int32 physical page ids; only the first
+ *               ceil(kv_lens[r] / page_size) entries of a row are read
+ *  kv_lens      [rows] int32 (device), each in [1, max_kv_len]
+ *  out          [rows, num_q_heads, head_dim] bf16, row stride out_row_stride
+ *  max_kv_len   an upper bound on every kv_lens[r]; it sizes the grid and the
+ *               workspace only -- results do not depend on it
+ *  workspace    >= decode_attn_workspace_size(rows, num_q_heads, head_dim,
+ *               max_kv_len, split_size) bytes, 16-byte aligned
+ * Supported: head_dim 64 or 128; page_size 16; split_size a positive multiple of
+ * page_size; num_q_heads % num_kv_heads == 0 with a group of 1..16 query heads;
+ * q, out 16-byte aligned with row strides multiples of 8.  A kv_lens entry
+ * outside [1, max_kv_len] is clamped into that range on the device (it cannot
+ * be reported from there); keep lengths valid.
+ */
+size_t decode_attn_workspace_size(int64_t rows, int num_q_heads, int head_dim, int max_kv_len,
+                                  int split_size);
+int decode_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, const void *v_cache,
+                   const int32_t *block_table, int64_t bt_stride, const int32_t *kv_lens,
+                   void *out, int64_t out_row_stride, int64_t rows, int num_q_heads,
+                   int num_kv_heads, int head_dim, int page_size, int split_size, int max_kv_len,
+                   float scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * decode_attn_tuned: same function, but the split size is chosen from the
+ * batch shape so that the splits fill the chip, the "balanced scheduling" of
+ * [P1] section 5.5 that the page names as not batch-invariant.
+ * decode_attn_tuned_split_size() returns the size it will use; kv_lens_host
+ * (optional, may be NULL) holds the rows' lengths on the host and sharpens the
+ * choice.  The workspace is sized with decode_attn_workspace_size(..., that
+ * split size).  Other arguments as decode_attn_bi.
+ */
+int decode_attn_tuned_split_size(int64_t rows, int num_kv_heads, int max_kv_len,
+                                 const int32_t *kv_lens_host);
+int decode_attn_tuned(const void *q, int64_t q_row_stride, const void *k_cache,
+                      const void *v_cache, const int32_t *block_table, int64_t bt_stride,
+                      const int32_t *kv_lens, const int32_t *kv_lens_host, void *out,
+                      int64_t out_row_stride, int64_t rows, int num_q_heads, int num_kv_heads,
+                      int head_dim, int page_size, int max_kv_len, float scale, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
+ * kv_append: write new tokens' K and V into their cache slots BEFORE attention
+ * runs, so cached and fresh tokens are reduced as one sequence with the same
+ * split boundaries ([P1] section 5.5: update the KV cache and page table before
+ * the attention kernel).  Token t goes to page slot_mapping[t] / page_size, slot
+ * slot_mapping[t] % page_size, for every kv head.
+ *  k_new, v_new  [tokens, num_kv_heads, head_dim] bf16, row strides
+ *                k_row_stride / v_row_stride (head stride head_dim)
+ *  slot_mapping  [tokens] int32 (device); an entry < 0 or >= num_pages*page_size
+ *                is skipped (no write)
+ * Requirements: 16-byte aligned pointers, head_dim a multiple of 8, row strides
+ * multiples of 8.
+ */
+int kv_append(const void *k_new, int64_t k_row_stride, const void *v_new, int64_t v_row_stride,
+              const int32_t *slot_mapping, int64_t tokens, void *k_cache, void *v_cache,
+              int64_t num_pages, int num_kv_heads, int head_dim, int page_size, void *stream);
+
+/* -------------------------------------------------------------------------- */
+/* Element-wise glue of a decode step (invariant by construction: no reduction */
+/* crosses rows; [P1] section 5.4)                                             */
+/* -------------------------------------------------------------------------- */
+/* out[r,:] = table[ids[r], :]; bf16, table [vocab, hidden]; an id outside
+ * [0, vocab) yields a zero row.  hidden a multiple of 8, 16-byte aligned. */
+int rbi_embed(const void *table, int64_t vocab, int64_t hidden, const int32_t *ids, int64_t rows,
+              void *out, int64_t out_row_stride, void *stream);
+
+/* out = bf16(float(a) + float(b)) over n contiguous bf16 elements (may alias). */
+int rbi_residual_add(const void *a, const void *b, void *out, int64_t n, void *stream);
+
+/* out[r,i] = bf16(silu(g) * u), g = gu[r, i], u = gu[r, inter + i], in fp32;
+ * silu(g) = g / (1 + exp(-g)).  gu [rows, 2*inter] bf16, out [rows, inter]. */
+int rbi_swiglu(const void *gu, int64_t gu_row_stride, void *out, int64_t out_row_stride,
+               int64_t rows, int64_t inter, void *stream);
+
+/* out[r] = index of the largest x[r, :] (fp32), the lowest index on ties; NaN
+ * entries are skipped (a row of only NaN yields 0). */
+int rbi_argmax_rows(const float *x, int64_t x_row_stride, int64_t rows, int64_t n,
+                    int32_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RBI_H */

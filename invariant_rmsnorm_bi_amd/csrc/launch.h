@@ -1,0 +1,69 @@
+// launch.h -- host-side launchers of the librbi kernels (internal; the public
+// boundary is include/rbi.h).  Arguments reaching these functions have already
+// been validated by capi.cpp; each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rbi {
+
+// rmsnorm.hip
+hipError_t launch_rmsnorm_wave(const void *x, int64_t xs, const void *w, void *y, int64_t ys,
+                               int64_t rows, int64_t hidden, float eps, bool bf16,
+                               hipStream_t s);
+hipError_t launch_rmsnorm_block(const void *x, int64_t xs, const void *w, void *y, int64_t ys,
+                                int64_t rows, int64_t hidden, float eps, bool bf16,
+                                hipStream_t s);
+
+// matmul.hip
+struct MatmulArgs {
+    const uint16_t *A;
+    int64_t lda;
+    const uint16_t *W;
+    int64_t ldw;
+    void *C;
+    int64_t ldc;
+    bool c_bf16;
+    int64_t M, N, K;
+};
+hipError_t launch_matmul_bi(const MatmulArgs &a, hipStream_t s);
+// split-K twin: `splits` partial products over equal K ranges into fp32 workspace
+// [splits, M, N], then an ascending-order reduction into C.
+hipError_t launch_matmul_splitk(const MatmulArgs &a, int splits, float *ws, hipStream_t s);
+int matmul_tuned_splits(int64_t M, int64_t N, int64_t K);
+
+// attention.hip
+struct AttnArgs {
+    const uint16_t *q;
+    int64_t q_row_stride;
+    const uint16_t *k_cache, *v_cache;
+    const int32_t *block_table;
+    int64_t bt_stride;
+    const int32_t *kv_lens;
+    uint16_t *out;
+    int64_t out_row_stride;
+    int64_t rows;
+    int hq, hkv, d, page, split, max_kv_len;
+    float scale;
+    float *ws;  // partials: [rows, hq, nsplit_max] x (D + 2) floats
+};
+size_t attn_workspace_bytes(int64_t rows, int hq, int d, int max_kv_len, int split);
+hipError_t launch_decode_attn(const AttnArgs &a, hipStream_t s);
+hipError_t launch_kv_append(const uint16_t *k_new, int64_t ks, const uint16_t *v_new, int64_t vs,
+                            const int32_t *slots, int64_t tokens, uint16_t *k_cache,
+                            uint16_t *v_cache, int64_t num_pages, int hkv, int d, int page,
+                            hipStream_t s);
+
+// glue.hip
+hipError_t launch_embed(const uint16_t *table, int64_t vocab, int64_t hidden, const int32_t *ids,
+                        int64_t rows, uint16_t *out, int64_t os, hipStream_t s);
+hipError_t launch_residual_add(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t n,
+                               hipStream_t s);
+hipError_t launch_swiglu(const uint16_t *gu, int64_t gs, uint16_t *out, int64_t os, int64_t rows,
+                         int64_t inter, hipStream_t s);
+hipError_t launch_argmax(const float *x, int64_t xs, int64_t rows, int64_t n, int32_t *out,
+                         hipStream_t s);
+
+}  // namespace rbi

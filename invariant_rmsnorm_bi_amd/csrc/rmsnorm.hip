@@ -1,0 +1,259 @@
+// rmsnorm.hip -- row-local RMSNorm for gfx950.
+//
+//   y[r,i] = (x[r,i] * rsq) * w[i],  rsq = 1 / sqrt(sum_j x[r,j]^2 / H + eps)
+//
+// Batch invariance ("Reproducible LLM Inference ...", hidekazu-konishi.com,
+// section 5.3: give each batch element its own core so its reduction never
+// splits): every row is reduced by exactly one wavefront, in an order that is
+// a function of H alone.
+//
+// Reduction order of one row (the contract of rmsnorm_bi):
+//   * the row is cut into 16-byte chunks (8 bf16 or 4 fp32 elements);
+//   * lane l owns chunks l, l+64, l+128, ... and keeps one fp32 partial per
+//     element slot e of a chunk, updated with fmaf(x, x, partial) over its
+//     chunks in ascending order;
+//   * the slot partials of a lane are added by a fixed pairwise tree;
+//   * the 64 lane sums are added by the xor butterfly (32, 16, ..., 1).
+// Keeping one partial per slot gives every lane several short chains, so a
+// large square cannot absorb a long run of small ones the way a single
+// sequential accumulator does (the failure worked through on the
+// praveentn.live page, "A Concrete Example").
+//
+// The twin (rmsnorm_tuned) spreads a row over a 256-thread workgroup when the
+// batch is too small to fill the chip: a different tree, hence different bits.
+#include "device.h"
+#include "launch.h"
+
+namespace rbi {
+namespace {
+
+template <bool BF16>
+struct Elt {
+    static constexpr int VEC = BF16 ? 8 : 4;    // elements per 16-byte chunk
+    static constexpr int SIZE = BF16 ? 2 : 4;   // bytes per element
+};
+
+// Chunk c of a row with H elements, widened to fp32; elements at or past H read as 0.
+template <bool BF16>
+__device__ __forceinline__ void load_chunk(const char *row, int64_t c, int64_t H, float *v)
+{
+    constexpr int VEC = Elt<BF16>::VEC;
+    const int64_t e0 = c * VEC;
+    if (e0 + VEC <= H) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(row + e0 * Elt<BF16>::SIZE);
+        if constexpr (BF16) {
+            unpack8(q, v);
+        } else {
+            v[0] = __uint_as_float(q.x);
+            v[1] = __uint_as_float(q.y);
+            v[2] = __uint_as_float(q.z);
+            v[3] = __uint_as_float(q.w);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int64_t i = e0 + e;
+            if (i < H) {
+                if constexpr (BF16)
+                    v[e] = bf16_to_f32(reinterpret_cast<const uint16_t *>(row)[i]);
+                else
+                    v[e] = reinterpret_cast<const float *>(row)[i];
+            } else {
+                v[e] = 0.f;
+            }
+        }
+    }
+}
+
+// y chunk = round((x * rsq) * w), elements past H are not written.
+template <bool BF16>
+__device__ __forceinline__ void store_chunk(char *row, const char *wrow, int64_t c, int64_t H,
+                                            const float *v, float rsq)
+{
+    constexpr int VEC = Elt<BF16>::VEC;
+    float w[VEC];
+    load_chunk<BF16>(wrow, c, H, w);
+    float o[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+        o[e] = (v[e] * rsq) * w[e];
+    const int64_t e0 = c * VEC;
+    if (e0 + VEC <= H) {
+        uint4 q;
+        if constexpr (BF16) {
+            q.x = pack_bf16x2(o[0], o[1]);
+            q.y = pack_bf16x2(o[2], o[3]);
+            q.z = pack_bf16x2(o[4], o[5]);
+            q.w = pack_bf16x2(o[6], o[7]);
+        } else {
+            q.x = __float_as_uint(o[0]);
+            q.y = __float_as_uint(o[1]);
+            q.z = __float_as_uint(o[2]);
+            q.w = __float_as_uint(o[3]);
+        }
+        *reinterpret_cast<uint4 *>(row + e0 * Elt<BF16>::SIZE) = q;
+    } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int64_t i = e0 + e;
+            if (i < H) {
+                if constexpr (BF16)
+                    reinterpret_cast<uint16_t *>(row)[i] = (uint16_t)f32_to_bf16(o[e]);
+                else
+                    reinterpret_cast<float *>(row)[i] = o[e];
+            }
+        }
+    }
+}
+
+// Fixed pairwise tree over the per-slot partials of one lane.
+template <int VEC>
+__device__ __forceinline__ float slot_tree(const float *p)
+{
+    if constexpr (VEC == 8)
+        return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    else
+        return (p[0] + p[1]) + (p[2] + p[3]);
+}
+
+__device__ __forceinline__ float inv_rms(float sumsq, int64_t H, float eps)
+{
+    const float ms = sumsq / (float)H;
+    return 1.0f / sqrtf(ms + eps);
+}
+
+// One wavefront per row, four rows per 256-thread workgroup.  Rows of up to
+// 64*CPL chunks stay in registers between the two passes; longer rows are read
+// twice.  Both paths execute the same arithmetic in the same order.
+template <bool BF16, int CPL>
+__global__ __launch_bounds__(256) void rmsnorm_wave_kernel(const char *x, int64_t xs,
+                                                           const char *__restrict__ w, char *y,
+                                                           int64_t ys, int64_t rows, int64_t H,
+                                                           float eps)
+{
+    constexpr int VEC = Elt<BF16>::VEC;
+    constexpr int SZ = Elt<BF16>::SIZE;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows)
+        return;
+    const char *xr = x + row * xs * SZ;
+    char *yr = y + row * ys * SZ;
+    const int64_t nchunks = (H + VEC - 1) / VEC;
+    float part[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+        part[e] = 0.f;
+
+    if (nchunks <= 64 * CPL) {
+        float v[CPL][VEC];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int64_t c = lane + 64 * i;
+            if (c < nchunks) {
+                load_chunk<BF16>(xr, c, H, v[i]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    v[i][e] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                part[e] = fmaf(v[i][e], v[i][e], part[e]);
+        const float rsq = inv_rms(wave_sum_butterfly(slot_tree<VEC>(part)), H, eps);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int64_t c = lane + 64 * i;
+            if (c < nchunks)
+                store_chunk<BF16>(yr, w, c, H, v[i], rsq);
+        }
+    } else {
+        for (int64_t c = lane; c < nchunks; c += 64) {
+            float v[VEC];
+            load_chunk<BF16>(xr, c, H, v);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                part[e] = fmaf(v[e], v[e], part[e]);
+        }
+        const float rsq = inv_rms(wave_sum_butterfly(slot_tree<VEC>(part)), H, eps);
+        for (int64_t c = lane; c < nchunks; c += 64) {
+            float v[VEC];
+            load_chunk<BF16>(xr, c, H, v);
+            store_chunk<BF16>(yr, w, c, H, v, rsq);
+        }
+    }
+}
+
+// Twin: one 256-thread workgroup per row.  Thread t owns chunks t, t+256, ...;
+// slot tree, wave butterfly, then the four wave sums ((w0 + w1) + (w2 + w3)).
+template <bool BF16>
+__global__ __launch_bounds__(256) void rmsnorm_block_kernel(const char *x, int64_t xs,
+                                                            const char *__restrict__ w, char *y,
+                                                            int64_t ys, int64_t rows, int64_t H,
+                                                            float eps)
+{
+    constexpr int VEC = Elt<BF16>::VEC;
+    constexpr int SZ = Elt<BF16>::SIZE;
+    __shared__ float wsum[4];
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const char *xr = x + row * xs * SZ;
+    char *yr = y + row * ys * SZ;
+    const int64_t nchunks = (H + VEC - 1) / VEC;
+    float part[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+        part[e] = 0.f;
+    for (int64_t c = t; c < nchunks; c += 256) {
+        float v[VEC];
+        load_chunk<BF16>(xr, c, H, v);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            part[e] = fmaf(v[e], v[e], part[e]);
+    }
+    const float s = wave_sum_butterfly(slot_tree<VEC>(part));
+    if ((t & 63) == 0)
+        wsum[t >> 6] = s;
+    __syncthreads();
+    const float rsq = inv_rms((wsum[0] + wsum[1]) + (wsum[2] + wsum[3]), H, eps);
+    for (int64_t c = t; c < nchunks; c += 256) {
+        float v[VEC];
+        load_chunk<BF16>(xr, c, H, v);
+        store_chunk<BF16>(yr, w, c, H, v, rsq);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm_wave(const void *x, int64_t xs, const void *w, void *y, int64_t ys,
+                               int64_t rows, int64_t hidden, float eps, bool bf16,
+                               hipStream_t s)
+{
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    if (bf16)
+        rmsnorm_wave_kernel<true, 8><<<grid, block, 0, s>>>(
+            (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
+    else
+        rmsnorm_wave_kernel<false, 8><<<grid, block, 0, s>>>(
+            (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_block(const void *x, int64_t xs, const void *w, void *y, int64_t ys,
+                                int64_t rows, int64_t hidden, float eps, bool bf16,
+                                hipStream_t s)
+{
+    const dim3 grid((unsigned)rows), block(256);
+    if (bf16)
+        rmsnorm_block_kernel<true><<<grid, block, 0, s>>>(
+            (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
+    else
+        rmsnorm_block_kernel<false><<<grid, block, 0, s>>>(
+            (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
+    return hipGetLastError();
+}
+
+}  // namespace rbi

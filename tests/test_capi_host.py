@@ -1,0 +1,149 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports every
+symbol include/rbi.h declares, and rejects bad arguments with the documented
+status before anything would be enqueued.  Only invalid calls are made here, so
+no kernel is ever launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import invariant_rmsnorm_bi_amd as rbi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rbi.h")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE = 0, -1, -2, -3
+NULL = None
+FAKE = 0x10000  # a 16-byte aligned, never-dereferenced stand-in pointer
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_and_binding_agree():
+    assert set(declared_functions()) == set(rbi.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = rbi.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_status_strings_and_version():
+    L = rbi.lib()
+    for st in (OK, EINVAL, EUNSUPPORTED, EWORKSPACE, -4, 7):
+        assert L.rbi_status_string(st)
+    assert L.rbi_status_string(EINVAL).startswith(b"RBI_EINVAL")
+    assert L.rbi_abi_version() == 1
+
+
+def test_rmsnorm_validation():
+    f = rbi.lib().rmsnorm_bi
+    assert f(FAKE, 8, FAKE, FAKE, 8, 0, 8, 1e-6, 1, NULL) == OK          # zero rows: no-op
+    assert f(FAKE, 8, FAKE, FAKE, 8, 4, 8, 1e-6, 7, NULL) == EUNSUPPORTED
+    assert f(NULL, 8, FAKE, FAKE, 8, 4, 8, 1e-6, 1, NULL) == EINVAL
+    assert f(FAKE + 2, 8, FAKE, FAKE, 8, 4, 8, 1e-6, 1, NULL) == EINVAL  # misaligned
+    assert f(FAKE, 12, FAKE, FAKE, 16, 4, 8, 1e-6, 1, NULL) == EINVAL    # stride not 16 B
+    assert f(FAKE, 8, FAKE, FAKE, 8, 4, 16, 1e-6, 1, NULL) == EINVAL     # stride < hidden
+    assert f(FAKE, 8, FAKE, FAKE, 8, -1, 8, 1e-6, 1, NULL) == EINVAL
+    assert f(FAKE, 8, FAKE, FAKE, 8, 4, 0, 1e-6, 1, NULL) == EINVAL
+    assert rbi.lib().rmsnorm_tuned(NULL, 8, FAKE, FAKE, 8, 4, 8, 1e-6, 1, NULL) == EINVAL
+
+
+def test_matmul_validation():
+    f = rbi.lib().matmul_bi
+    assert f(FAKE, 64, FAKE, 64, FAKE, 64, 1, 0, 64, 64, NULL) == OK
+    assert f(FAKE, 64, FAKE, 64, FAKE, 64, 5, 4, 64, 64, NULL) == EUNSUPPORTED
+    assert f(FAKE, 64, FAKE, 64, FAKE, 64, 1, 4, 64, 60, NULL) == EINVAL   # K % 8
+    assert f(FAKE, 64, FAKE, 64, FAKE, 64, 1, 4, 62, 64, NULL) == EINVAL   # N % 4
+    assert f(FAKE, 60, FAKE, 64, FAKE, 64, 1, 4, 64, 64, NULL) == EINVAL   # lda < K
+    assert f(FAKE, 64, NULL, 64, FAKE, 64, 1, 4, 64, 64, NULL) == EINVAL
+    assert f(FAKE, 64, FAKE, 64, FAKE + 8, 64, 1, 4, 64, 64, NULL) == EINVAL
+    assert f(FAKE, 64, FAKE, 64, FAKE, 32, 1, 4, 64, 64, NULL) == EINVAL  # ldc < N
+    g = rbi.lib().matmul_tuned
+    need = rbi.matmul_tuned_workspace_size(1, 4096, 8192)
+    assert need > 0
+    assert g(FAKE, 8192, FAKE, 8192, FAKE, 4096, 1, 1, 4096, 8192, NULL, need, NULL) == EWORKSPACE
+    assert g(FAKE, 8192, FAKE, 8192, FAKE, 4096, 1, 1, 4096, 8192, FAKE, need - 1, NULL) == EWORKSPACE
+
+
+def test_matmul_tuned_workspace_shape_dependence():
+    # the twin splits K only when the output tiles cannot fill the chip
+    assert rbi.matmul_tuned_workspace_size(4096, 9216, 4096) == 0
+    assert rbi.matmul_tuned_workspace_size(1, 9216, 4096) > 0
+    assert rbi.matmul_tuned_workspace_size(0, 9216, 4096) == 0
+
+
+def _attn(**kw):
+    a = dict(q=FAKE, qs=64 * 128, kc=FAKE, vc=FAKE, bt=FAKE, bts=2048, lens=FAKE, out=FAKE,
+             os=64 * 128, rows=4, hq=64, hkv=4, d=128, page=16, split=256, maxlen=32768,
+             scale=0.088, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return rbi.lib().decode_attn_bi(a["q"], a["qs"], a["kc"], a["vc"], a["bt"], a["bts"],
+                                    a["lens"], a["out"], a["os"], a["rows"], a["hq"], a["hkv"],
+                                    a["d"], a["page"], a["split"], a["maxlen"], a["scale"],
+                                    a["ws"], a["wsb"], NULL)
+
+
+def test_decode_attn_validation():
+    assert _attn(rows=0) == OK
+    assert _attn(d=96) == EUNSUPPORTED
+    assert _attn(page=32) == EUNSUPPORTED
+    assert _attn(split=250) == EUNSUPPORTED        # not a multiple of the page
+    assert _attn(hq=64, hkv=2) == EUNSUPPORTED      # group of 32 query heads
+    assert _attn(hq=63) == EINVAL                   # not a multiple of hkv
+    assert _attn(maxlen=0) == EINVAL
+    assert _attn(bts=100) == EINVAL                 # table too narrow for max_kv_len
+    assert _attn(q=NULL) == EINVAL
+    assert _attn(lens=NULL) == EINVAL
+    assert _attn(out=FAKE + 4) == EINVAL
+    assert _attn(qs=64 * 128 - 8) == EINVAL
+    assert _attn(ws=NULL) == EWORKSPACE
+    need = rbi.decode_attn_workspace_size(4, 64, 128, 32768, 256)
+    assert need == 4 * 64 * 128 * 130 * 4
+    assert _attn(wsb=need - 1) == EWORKSPACE
+
+
+def test_decode_attn_workspace_depends_only_on_bounds():
+    a = rbi.decode_attn_workspace_size(256, 64, 128, 32768, 256)
+    assert a == 256 * 64 * 128 * (128 + 2) * 4
+    assert rbi.decode_attn_workspace_size(5, 4, 64, 63, 16) == 5 * 4 * 4 * 66 * 4
+
+
+def test_tuned_split_size_follows_the_batch():
+    # balanced scheduling: long single request -> small splits; big batch -> large
+    one = rbi.decode_attn_tuned_split_size(1, 4, 32768, [32768])
+    many = rbi.decode_attn_tuned_split_size(256, 4, 32768, [32768] * 256)
+    assert one <= 256 and many >= 4096
+    assert one % 16 == 0 and many % 16 == 0
+    # the fixed-size kernel would use 256 in both cases
+
+
+def test_kv_append_and_glue_validation():
+    L = rbi.lib()
+    assert L.kv_append(FAKE, 512, FAKE, 512, FAKE, 0, FAKE, FAKE, 10, 4, 128, 16, NULL) == OK
+    assert L.kv_append(FAKE, 512, FAKE, 512, NULL, 3, FAKE, FAKE, 10, 4, 128, 16, NULL) == EINVAL
+    assert L.kv_append(FAKE, 500, FAKE, 512, FAKE, 3, FAKE, FAKE, 10, 4, 128, 16, NULL) == EINVAL
+    assert L.rbi_embed(FAKE, 100, 64, NULL, 3, FAKE, 64, NULL) == EINVAL
+    assert L.rbi_embed(FAKE, 100, 60, FAKE, 3, FAKE, 64, NULL) == EINVAL
+    assert L.rbi_residual_add(FAKE, FAKE, FAKE, 0, NULL) == OK
+    assert L.rbi_residual_add(NULL, FAKE, FAKE, 8, NULL) == EINVAL
+    assert L.rbi_swiglu(FAKE, 10, FAKE, 5, 3, 6, NULL) == EINVAL
+    assert L.rbi_argmax_rows(FAKE, 10, 3, 20, FAKE, NULL) == EINVAL
+    assert L.rbi_argmax_rows(NULL, 10, 3, 10, FAKE, NULL) == EINVAL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 8, dtype=torch.bfloat16)
+    with pytest.raises(rbi.RbiError):
+        rbi.rmsnorm_bi(x, torch.ones(8, dtype=torch.bfloat16))

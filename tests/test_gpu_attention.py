@@ -1,0 +1,262 @@
+"""GPU tests of decode_attn_bi / decode_attn_tuned / kv_append: parity with the
+CPU oracle (max|out - ref| <= 2e-2 * RMS(ref)) and bitwise invariance across
+batch size, neighbours, order, page placement, grid extent (max_kv_len), KV
+growth across split boundaries and chunked versus unchunked prefill.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_rmsnorm_bi_amd as rbi
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _to(kv: synth.PagedKV) -> synth.PagedKV:
+    return synth.PagedKV(kv.k_cache.to(DEV), kv.v_cache.to(DEV), kv.block_table.to(DEV),
+                         kv.kv_lens.to(DEV), kv.page_size, kv.num_kv_heads, kv.head_dim,
+                         kv.extra)
+
+
+def _oracle(q, kv, scale, rows=None):
+    bt = kv.block_table.cpu().numpy()
+    lens = kv.kv_lens.cpu().numpy()
+    qb = synth.bf16_bits(q.cpu())
+    if rows is not None:
+        bt, lens, qb = bt[rows], lens[rows], qb[rows]
+    return oracle.decode_attn(qb, synth.bf16_bits(kv.k_cache.cpu()),
+                              synth.bf16_bits(kv.v_cache.cpu()), bt, lens, scale)
+
+
+def _tol_ok(out, ref):
+    err = np.abs(out.double().cpu().numpy() - ref).max()
+    rms = np.sqrt(np.mean(ref ** 2))
+    return err <= 2e-2 * rms, err, rms
+
+
+def _run(fn, q, kv, max_len, **kw):
+    return fn(q, kv.k_cache, kv.v_cache, kv.block_table, kv.kv_lens, max_len, **kw)
+
+
+def test_c1_tiny_parity_and_rows_bitwise():
+    # 4 query heads over 1 kv head, head_dim 64, lengths {5, 17, 63}, page 16, split 16
+    lens = [5, 17, 63]
+    kv = _to(synth.paged_kv(lens, 1, 64, 16))
+    q = synth.normal((3, 4, 64), seed=100).to(DEV)
+    scale = 1 / 8
+    out = _run(rbi.decode_attn_bi, q, kv, 63, split_size=16, scale=scale)
+    ok, err, rms = _tol_ok(out, _oracle(q, kv, scale))
+    assert ok, (err, rms)
+    assert not torch.isnan(out.float()).any()
+    for r in range(3):
+        sub = synth.PagedKV(kv.k_cache, kv.v_cache, kv.block_table[r:r + 1].contiguous(),
+                            kv.kv_lens[r:r + 1].contiguous(), 16, 1, 64)
+        alone = _run(rbi.decode_attn_bi, q[r:r + 1].contiguous(), sub, 63, split_size=16,
+                     scale=scale)
+        assert torch.equal(alone[0], out[r])
+    perm = [2, 0, 1]
+    sub = synth.PagedKV(kv.k_cache, kv.v_cache, kv.block_table[perm].contiguous(),
+                        kv.kv_lens[perm].contiguous(), 16, 1, 64)
+    shuf = _run(rbi.decode_attn_bi, q[perm].contiguous(), sub, 63, split_size=16, scale=scale)
+    assert torch.equal(shuf, out[perm])
+
+
+@pytest.mark.parametrize("lens", [[1], [255, 256, 257, 512, 513], [1, 2, 15, 16, 17, 31, 33],
+                                  [1999, 700, 64, 1040]])
+def test_c4_heads_parity(lens):
+    # 64 query heads over 4 kv heads, head_dim 128, page 16, split 256
+    kv = _to(synth.paged_kv(lens, 4, 128, 16))
+    q = synth.normal((len(lens), 64, 128), seed=3).to(DEV)
+    scale = 1 / math.sqrt(128)
+    ref = _oracle(q, kv, scale)
+    for fn, kw in ((rbi.decode_attn_bi, dict(split_size=256)), (rbi.decode_attn_tuned, {})):
+        out = _run(fn, q, kv, max(lens), scale=scale, **kw)
+        ok, err, rms = _tol_ok(out, ref)
+        assert ok, (fn.__name__, err, rms)
+
+
+def test_single_token_is_exact():
+    # L = 1: the softmax weight is exactly 1, so the output is v_0 bit for bit
+    kv = _to(synth.paged_kv([1, 1, 1], 4, 128, 16))
+    q = synth.normal((3, 64, 128), seed=4).to(DEV)
+    out = _run(rbi.decode_attn_bi, q, kv, 1)
+    for r in range(3):
+        p = int(kv.block_table[r, 0])
+        v0 = kv.v_cache[p, :, 0, :]                       # [4, 128]
+        assert torch.equal(out[r], v0.repeat_interleave(16, 0))
+
+
+def test_c4_full_batch_sampled_parity_and_batch_invariance():
+    # batch 256 with lengths ~ U{1..32768}, split 256; oracle on sampled rows
+    lens = synth.uniform_lengths(256, 1, 32768)
+    kv = synth.paged_kv(lens, 4, 128, 16, max_pages=2048, device=DEV)
+    q = synth.normal((256, 64, 128), seed=5).to(DEV)
+    scale = 1 / math.sqrt(128)
+    out = _run(rbi.decode_attn_bi, q, kv, 32768)
+    rows = [0, 17, 100, 255]
+    ok, err, rms = _tol_ok(out[rows], _oracle(q, kv, scale, rows=rows))
+    assert ok, (err, rms)
+    # every row alone and in random sub-batches gives the same bits
+    rng = np.random.default_rng(synth.SEED_BATCH)
+    for B in (1, 2, 3, 7, 16, 64, 255):
+        members = synth.batch_members(256, B, seed=int(rng.integers(1 << 30)))
+        idx = torch.tensor(members, device=DEV)
+        sub = synth.PagedKV(kv.k_cache, kv.v_cache, kv.block_table[idx].contiguous(),
+                            kv.kv_lens[idx].contiguous(), 16, 4, 128)
+        o = _run(rbi.decode_attn_bi, q[idx].contiguous(), sub, 32768)
+        assert torch.equal(o, out[idx]), B
+
+
+def test_grid_extent_and_page_placement_do_not_matter():
+    lens = [300, 1000, 77]
+    a = synth.paged_kv(lens, 4, 128, 16, seed=0, page_seed=3)
+    b = synth.paged_kv(lens, 4, 128, 16, seed=0, page_seed=99)
+    for r, L in enumerate(lens):       # same logical content, other physical pages
+        for j in range(-(-L // 16)):
+            b.k_cache[int(b.block_table[r, j])] = a.k_cache[int(a.block_table[r, j])]
+            b.v_cache[int(b.block_table[r, j])] = a.v_cache[int(a.block_table[r, j])]
+    a, b = _to(a), _to(b)
+    q = synth.normal((3, 64, 128), seed=6).to(DEV)
+    o1 = _run(rbi.decode_attn_bi, q, a, 1000)
+    o2 = _run(rbi.decode_attn_bi, q, b, 1000)
+    assert torch.equal(o1, o2)
+    wide = torch.full((3, 2048), int(a.extra["poison_page"]), dtype=torch.int32, device=DEV)
+    wide[:, : a.block_table.shape[1]] = a.block_table
+    a2 = synth.PagedKV(a.k_cache, a.v_cache, wide, a.kv_lens, 16, 4, 128)
+    o3 = _run(rbi.decode_attn_bi, q, a2, 32768)       # larger grid and workspace
+    assert torch.equal(o1, o3)
+
+
+def test_kv_growth_across_split_boundaries():
+    # one request grows by one token per step from 240 to 1040 tokens, crossing the
+    # 256/512/768/1024 boundaries; at every length its output in a random batch equals
+    # its output alone, and the partials of completed splits never change
+    D, HKV, HQ, S = 128, 4, 64, 256
+    pool_lens = synth.uniform_lengths(32, 1, 4096, seed=77)
+    others = synth.paged_kv(pool_lens, HKV, D, 16, seed=7)
+    probe = synth.paged_kv([1040], HKV, D, 16, seed=8, page_seed=9)
+    q = synth.normal((1, HQ, D), seed=10).to(DEV)
+    qo = synth.normal((32, HQ, D), seed=11).to(DEV)
+    # one cache holding both: probe pages appended after the others'
+    n_o = others.k_cache.shape[0]
+    kc = torch.cat([others.k_cache, probe.k_cache]).to(DEV)
+    vc = torch.cat([others.v_cache, probe.v_cache]).to(DEV)
+    bt_p = probe.block_table + n_o
+    maxp = 4096 // 16
+    bt_o = torch.full((32, maxp), int(others.extra["poison_page"]), dtype=torch.int32)
+    bt_o[:, : others.block_table.shape[1]] = others.block_table
+    bt_pp = torch.full((1, maxp), n_o + int(probe.extra["poison_page"]), dtype=torch.int32)
+    bt_pp[:, : bt_p.shape[1]] = bt_p
+    rng = np.random.default_rng(12)
+    done_partials = {}
+    for L in range(240, 1041):
+        lens1 = torch.tensor([L], dtype=torch.int32, device=DEV)
+        ws1 = torch.zeros(rbi.decode_attn_workspace_size(1, HQ, D, 4096, S), dtype=torch.uint8,
+                          device=DEV)
+        alone = rbi.decode_attn_bi(q, kc, vc, bt_pp.to(DEV), lens1, 4096, S, workspace=ws1)
+        # partials of splits that ended before L: bit-identical at every later length
+        nsmax = 4096 // S
+        acc = ws1[: HQ * nsmax * D * 4].view(torch.float32).view(HQ, nsmax, D)
+        for s in range(L // S):
+            if s in done_partials:
+                assert torch.equal(acc[:, s], done_partials[s]), (L, s)
+            else:
+                done_partials[s] = acc[:, s].clone()
+        B = int(rng.integers(2, 33))
+        pos = int(rng.integers(0, B))
+        mem = rng.choice(32, size=B - 1, replace=False)
+        qb = torch.cat([qo[mem[:pos]], q, qo[mem[pos:]]])
+        btb = torch.cat([bt_o[mem[:pos]], bt_pp, bt_o[mem[pos:]]]).to(DEV)
+        lb = torch.tensor([pool_lens[i] for i in mem[:pos]] + [L] +
+                          [pool_lens[i] for i in mem[pos:]], dtype=torch.int32, device=DEV)
+        ob = rbi.decode_attn_bi(qb, kc, vc, btb, lb, 4096, S)
+        assert torch.equal(ob[pos], alone[0]), L
+
+
+def test_chunked_prefill_equals_unchunked():
+    # a 700-token prompt: append all K/V then attend every token (row p sees p+1
+    # tokens), versus seeded random chunks, each appended before its rows attend
+    T, HKV, HQ, D = 700, 4, 64, 128
+    npages = -(-T // 16)
+    pages = synth.page_ids(npages + 8, seed=13)[:npages].to(DEV)
+    k_new = synth.normal((T, HKV, D), seed=14).to(DEV)
+    v_new = synth.normal((T, HKV, D), seed=15).to(DEV)
+    q = synth.normal((T, HQ, D), seed=16).to(DEV)
+    slots = (pages[torch.arange(T, device=DEV) // 16] * 16 +
+             torch.arange(T, device=DEV) % 16).to(torch.int32)
+    bt = pages[None].repeat(T, 1).to(torch.int32).contiguous()
+
+    def fresh():
+        return (torch.full((npages + 8, HKV, 16, D), float("nan"), dtype=torch.bfloat16, device=DEV),
+                torch.full((npages + 8, HKV, 16, D), float("nan"), dtype=torch.bfloat16, device=DEV))
+
+    kc, vc = fresh()
+    rbi.kv_append(k_new, v_new, slots, kc, vc)
+    lens = torch.arange(1, T + 1, dtype=torch.int32, device=DEV)
+    full = rbi.decode_attn_bi(q, kc, vc, bt, lens, T, 256)
+    kc2, vc2 = fresh()
+    rng = np.random.default_rng(17)
+    cuts = sorted(set(rng.integers(1, T, size=9).tolist()))
+    bounds = [0] + cuts + [T]
+    chunked = torch.empty_like(full)
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        rbi.kv_append(k_new[a:b], v_new[a:b], slots[a:b].contiguous(), kc2, vc2)
+        chunked[a:b] = rbi.decode_attn_bi(q[a:b].contiguous(), kc2, vc2, bt[a:b].contiguous(),
+                                          lens[a:b].contiguous(), T, 256)
+    assert torch.equal(full, chunked)
+    assert not torch.isnan(full.float()).any()
+
+
+def test_kv_append_exact_placement():
+    T, HKV, D = 37, 4, 128
+    kc = torch.zeros((20, HKV, 16, D), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    k_new = synth.normal((T, HKV * D), seed=18).to(DEV)
+    v_new = synth.normal((T, HKV * D), seed=19).to(DEV)
+    slots = torch.randperm(20 * 16, generator=synth.gen(20))[:T].to(torch.int32)
+    slots[5] = -1                      # skipped
+    slots[6] = 20 * 16                 # out of range: skipped
+    rbi.kv_append(k_new, v_new, slots.to(DEV), kc, vc)
+    kc_h, vc_h = kc.cpu(), vc.cpu()
+    kn, vn = k_new.cpu().view(T, HKV, D), v_new.cpu().view(T, HKV, D)
+    written = torch.zeros(20 * 16, dtype=torch.bool)
+    for t in range(T):
+        s = int(slots[t])
+        if 0 <= s < 320:
+            assert torch.equal(kc_h[s // 16, :, s % 16], kn[t])
+            assert torch.equal(vc_h[s // 16, :, s % 16], vn[t])
+            written[s] = True
+    flat = kc_h.permute(0, 2, 1, 3).reshape(320, -1)
+    assert float(flat[~written].abs().max()) == 0
+
+
+def test_tuned_twin_sensitivity():
+    # the balanced twin picks a different split size for a lone long request than
+    # for a full batch, so the probe's bits move
+    lens = synth.uniform_lengths(256, 1, 32768, seed=21)
+    lens[0] = 20000
+    kv = synth.paged_kv(lens, 4, 128, 16, max_pages=2048, device=DEV)
+    q = synth.normal((256, 64, 128), seed=22).to(DEV)
+    full = rbi.decode_attn_tuned(q, kv.k_cache, kv.v_cache, kv.block_table, kv.kv_lens, 32768,
+                                 kv_lens_host=lens)
+    one = rbi.decode_attn_tuned(q[:1], kv.k_cache, kv.v_cache, kv.block_table[:1].contiguous(),
+                                kv.kv_lens[:1].contiguous(), 32768, kv_lens_host=lens[:1])
+    assert rbi.decode_attn_tuned_split_size(1, 4, 32768, lens[:1]) != \
+        rbi.decode_attn_tuned_split_size(256, 4, 32768, lens)
+    assert not torch.equal(full[0], one[0])
+
+
+def test_run_to_run_200():
+    lens = synth.uniform_lengths(64, 1, 8192, seed=23)
+    kv = _to(synth.paged_kv(lens, 4, 128, 16, max_pages=8192 // 16))
+    q = synth.normal((64, 64, 128), seed=24).to(DEV)
+    ref = _run(rbi.decode_attn_bi, q, kv, 8192)
+    diff = torch.zeros((), dtype=torch.int64, device=DEV)
+    for _ in range(200):
+        diff += (_run(rbi.decode_attn_bi, q, kv, 8192) != ref).sum()
+    assert int(diff) == 0

@@ -1,0 +1,168 @@
+"""GPU tests of matmul_bi / matmul_tuned: parity with the CPU oracle (exact on
+integer inputs, max|C - ref| <= 2e-2 * RMS(ref) on normal inputs) and bitwise
+batch invariance over M, position and neighbours.
+"""
+import numpy as np
+import pytest
+import torch
+
+import invariant_rmsnorm_bi_amd as rbi
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+QKV = (9216, 4096)     # [N, K] of the attention QKV projection
+OPROJ = (4096, 8192)   # [N, K] of o_proj
+
+
+def _tol_ok(c: torch.Tensor, ref: np.ndarray) -> tuple:
+    err = np.abs(c.double().cpu().numpy() - ref).max()
+    rms = np.sqrt(np.mean(ref ** 2))
+    return err <= 2e-2 * rms, err, rms
+
+
+def test_c1_parity_and_rows_bitwise_across_batch():
+    A = synth.normal((8, 256), seed=synth.SEED_DATA)
+    W = synth.normal((512, 256), std=0.02, seed=synth.SEED_WEIGHTS)
+    ref = oracle.matmul(synth.bf16_bits(A), synth.bf16_bits(W))
+    Ag, Wg = A.to(DEV), W.to(DEV)
+    outs = {}
+    for B in (1, 3, 8):
+        c = rbi.matmul_bi(Ag[:B].contiguous(), Wg)
+        ok, err, rms = _tol_ok(c, ref[:B])
+        assert ok, (B, err, rms)
+        outs[B] = c
+    assert torch.equal(outs[3][:1], outs[1]) and torch.equal(outs[8][:3], outs[3])
+    for r in range(8):
+        assert torch.equal(rbi.matmul_bi(Ag[r:r + 1].contiguous(), Wg)[0], outs[8][r])
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 512, 256), (17, 4096, 4096), (130, 260, 1032),
+                                   (257, 9216, 512), (64, 128, 8)])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_integer_inputs_exact(M, N, K, out_dtype):
+    # integers in [-4, 4]: every partial sum is an integer below 2^24, so fp32 is exact
+    # in any order and the result must equal the oracle's rounded value bit for bit
+    A = synth.integer_valued((M, K), seed=M + K)
+    W = synth.integer_valued((N, K), seed=N + 1)
+    ref = oracle.matmul(synth.bf16_bits(A), synth.bf16_bits(W))
+    c = rbi.matmul_bi(A.to(DEV), W.to(DEV), out_dtype=out_dtype).cpu()
+    if out_dtype == torch.float32:
+        assert np.array_equal(c.double().numpy(), ref)
+    else:
+        assert np.array_equal(synth.bf16_bits(c), oracle.round_bf16(ref))
+    ct = rbi.matmul_tuned(A.to(DEV), W.to(DEV), out_dtype=out_dtype).cpu()
+    assert torch.equal(ct, c)
+
+
+@pytest.mark.parametrize("shape", [QKV, OPROJ])
+@pytest.mark.parametrize("M", [1, 7, 64, 127, 256])
+def test_c3_parity_normal_inputs(shape, M):
+    N, K = shape
+    A = synth.normal((M, K), seed=1000 + M)   # not a weight seed: keeps A and W independent
+    W = synth.normal((N, K), std=0.02, seed=synth.SEED_WEIGHTS)
+    ref = oracle.matmul(synth.bf16_bits(A), synth.bf16_bits(W))
+    Ag, Wg = A.to(DEV), W.to(DEV)
+    for fn in (rbi.matmul_bi, rbi.matmul_tuned):
+        ok, err, rms = _tol_ok(fn(Ag, Wg), ref)
+        assert ok, (fn.__name__, err, rms)
+
+
+@pytest.mark.parametrize("shape", [QKV, OPROJ])
+def test_c3_sampled_rows_at_m4096(shape):
+    N, K = shape
+    M = 4096
+    A = synth.normal((M, K), seed=11)
+    W = synth.normal((N, K), std=0.02, seed=synth.SEED_WEIGHTS)
+    c = rbi.matmul_bi(A.to(DEV), W.to(DEV))
+    rows = [0, 1, 127, 128, 2047, 4095]
+    ref = oracle.matmul(synth.bf16_bits(A[rows]), synth.bf16_bits(W))
+    ok, err, rms = _tol_ok(c[rows], ref)
+    assert ok, (err, rms)
+
+
+@pytest.mark.parametrize("shape", [QKV, OPROJ])
+def test_every_position_same_bits(shape):
+    # one row repeated M = 4096 times: every tile, wave and MFMA slot must produce the
+    # bits the row gets alone
+    N, K = shape
+    p = synth.normal((1, K), seed=21).to(DEV)
+    W = synth.normal((N, K), std=0.02, seed=synth.SEED_WEIGHTS).to(DEV)
+    alone = rbi.matmul_bi(p, W)
+    full = rbi.matmul_bi(p.repeat(4096, 1), W)
+    assert torch.equal(full, alone.expand_as(full))
+
+
+@pytest.mark.parametrize("shape", [QKV, OPROJ])
+def test_rows_bitwise_over_m_sweep(shape):
+    # M = 1..4096 (every value: odd, prime and tile-straddling M included); probe rows
+    # at the first, last and a seeded random position among N(0,1) neighbours
+    N, K = shape
+    pool = synth.normal((4096, K), seed=31).to(DEV)
+    W = synth.normal((N, K), std=0.02, seed=synth.SEED_WEIGHTS).to(DEV)
+    probe = synth.normal((1, K), seed=32).to(DEV)
+    alone = rbi.matmul_bi(probe, W)[0]
+    out = torch.empty((4096, N), dtype=torch.bfloat16, device=DEV)
+    rng = np.random.default_rng(synth.SEED_BATCH)
+    bad = torch.zeros((), dtype=torch.int64, device=DEV)
+    for M in range(1, 4097):
+        pos = int(rng.integers(0, M)) if M % 3 else (M - 1 if M % 2 else 0)
+        keep = pool[pos].clone()
+        pool[pos] = probe[0]
+        rbi.matmul_bi(pool[:M], W, out=out[:M])
+        bad += (out[pos] != alone).sum()
+        pool[pos] = keep
+    assert int(bad) == 0
+
+
+def test_p1_batch_slice_example():
+    # hidekazu-konishi.com section 3.3: row 0 of a[:1] @ b versus row 0 of a @ b with
+    # linspace matrices (here bf16 inputs, fp32 output, b stored as W = b^T [N, K]).
+    # The invariant kernel must give exactly 0 difference.
+    B, D = 2048, 4096
+    a = synth.linspace_matrix(B, D, dtype=torch.bfloat16).to(DEV)
+    W = synth.linspace_matrix(D, D, dtype=torch.bfloat16).T.contiguous().to(DEV)
+    one = rbi.matmul_bi(a[:1], W, out_dtype=torch.float32)
+    full = rbi.matmul_bi(a, W, out_dtype=torch.float32)[:1]
+    assert float((one - full).abs().max()) == 0.0
+    # the split-K twin is free to change with the batch: it splits K at M = 1 only
+    t_one = rbi.matmul_tuned(a[:1], W, out_dtype=torch.float32)
+    t_full = rbi.matmul_tuned(a, W, out_dtype=torch.float32)[:1]
+    assert float((t_one - t_full).abs().max()) > 0.0, "inputs lack the power to show a change"
+
+
+def test_tuned_twin_sensitivity_normal_inputs():
+    N, K = OPROJ
+    pool = synth.normal((4096, K), seed=41).to(DEV)
+    W = synth.normal((N, K), std=0.02, seed=synth.SEED_WEIGHTS).to(DEV)
+    small = rbi.matmul_tuned(pool[:1], W, out_dtype=torch.float32)
+    big = rbi.matmul_tuned(pool, W, out_dtype=torch.float32)[:1]
+    assert not torch.equal(small, big)
+    assert torch.equal(rbi.matmul_bi(pool[:1], W, out_dtype=torch.float32),
+                       rbi.matmul_bi(pool, W, out_dtype=torch.float32)[:1])
+
+
+def test_run_to_run_1000():
+    # hidekazu-konishi.com section 4.2: the same bf16 2048x2048 product 1000 times
+    A = synth.normal((2048, 2048), seed=51).to(DEV)
+    W = synth.normal((2048, 2048), seed=52).to(DEV)
+    ref = rbi.matmul_bi(A, W)
+    out = torch.empty_like(ref)
+    diff = torch.zeros((), dtype=torch.int64, device=DEV)
+    for _ in range(1000):
+        rbi.matmul_bi(A, W, out=out)
+        diff += (out != ref).sum()
+    assert int(diff) == 0
+
+
+def test_strided_views():
+    # A and C as column slices of wider buffers (row strides > K, > N)
+    A = synth.normal((40, 512), seed=61).to(DEV)
+    W = synth.normal((96, 256), std=0.02, seed=62).to(DEV)
+    out = torch.zeros((40, 200), dtype=torch.float32, device=DEV)
+    c = rbi.matmul_bi(A[:, 128:384], W, out_dtype=torch.float32, out=out[:, 100:196])
+    ref = oracle.matmul(synth.bf16_bits(A[:, 128:384].contiguous()), synth.bf16_bits(W))
+    ok, err, rms = _tol_ok(c, ref)
+    assert ok
+    assert float(out[:, :100].abs().max()) == 0 and float(out[:, 196:].abs().max()) == 0
