@@ -124,7 +124,19 @@ def _dtype_code(t: torch.Tensor) -> int:
 def _row_stride(t: torch.Tensor) -> int:
     if t.dim() < 2 or t.stride(-1) != 1:
         raise RbiError("expected a 2-D view with unit stride in the last dimension")
-    return t.stride(-2)
+    return _lead_stride(t)
+
+
+def _lead_stride(t: torch.Tensor) -> int:
+    """Stride of dimension 0 in elements.  A size-1 leading dimension may carry any
+    stride (numpy's newaxis gives 0); only row 0 is read then, so report the packed
+    row length instead."""
+    if t.shape[0] > 1:
+        return t.stride(0)
+    n = 1
+    for s in t.shape[1:]:
+        n *= s
+    return max(n, 1)
 
 
 # -------------------------------------------------------------------------------------
@@ -250,9 +262,9 @@ def decode_attn_bi(q, k_cache, v_cache, block_table, kv_lens, max_kv_len: int,
     need = decode_attn_workspace_size(rows, hq, d, max_kv_len, split_size)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    st = lib().decode_attn_bi(_ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache),
-                              _ptr(block_table), block_table.stride(0), _ptr(kv_lens), _ptr(out),
-                              out.stride(0), rows, hq, hkv, d, page, split_size, max_kv_len,
+    st = lib().decode_attn_bi(_ptr(q), _lead_stride(q), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(block_table), _lead_stride(block_table), _ptr(kv_lens),
+                              _ptr(out), _lead_stride(out), rows, hq, hkv, d, page, split_size, max_kv_len,
                               float(scale), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream())
     _check(st, "decode_attn_bi")
@@ -272,9 +284,9 @@ def decode_attn_tuned(q, k_cache, v_cache, block_table, kv_lens, max_kv_len: int
     need = decode_attn_workspace_size(rows, hq, d, max_kv_len, split)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    st = lib().decode_attn_tuned(_ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache),
-                                 _ptr(block_table), block_table.stride(0), _ptr(kv_lens),
-                                 _ptr(host), _ptr(out), out.stride(0), rows, hq, hkv, d, page,
+    st = lib().decode_attn_tuned(_ptr(q), _lead_stride(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(block_table), _lead_stride(block_table), _ptr(kv_lens),
+                                 _ptr(host), _ptr(out), _lead_stride(out), rows, hq, hkv, d, page,
                                  max_kv_len, float(scale), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream())
     _check(st, "decode_attn_tuned")
@@ -289,7 +301,7 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache) -> None:
     tokens = k_new.shape[0]
     if slot_mapping.dtype != torch.int32 or slot_mapping.shape[0] != tokens:
         raise RbiError("slot_mapping must be int32 [tokens]")
-    st = lib().kv_append(_ptr(k_new), k_new.stride(0), _ptr(v_new), v_new.stride(0),
+    st = lib().kv_append(_ptr(k_new), _lead_stride(k_new), _ptr(v_new), _lead_stride(v_new),
                          _ptr(slot_mapping), tokens, _ptr(k_cache), _ptr(v_cache), num_pages, hkv,
                          d, page, _stream())
     _check(st, "kv_append")

@@ -61,9 +61,11 @@ class DenseLayerOracle:
         self.k_cache = np.zeros(shape, dtype=np.uint16)
         self.v_cache = np.zeros(shape, dtype=np.uint16)
 
-    def step(self, tokens, block_tables: np.ndarray, positions) -> tuple[np.ndarray, np.ndarray]:
+    def step(self, tokens, block_tables: np.ndarray, positions,
+             logit_rows=None) -> tuple[np.ndarray, np.ndarray]:
         """One decode step for rows (token, block table row, position).  Returns
-        (fp32 logits [B, vocab], argmax tokens [B])."""
+        (fp32 logits, argmax tokens) for the rows listed in ``logit_rows`` (all rows
+        by default); the other rows still update the cache."""
         d = self.d
         tokens = np.asarray(tokens, dtype=np.int64)
         positions = np.asarray(positions, dtype=np.int64)
@@ -93,6 +95,8 @@ class DenseLayerOracle:
         s = round_bf16(silu_mul(g, u))
         dn = round_bf16(matmul(s, self.w["wd"]))
         o2 = round_bf16(bf16_to_f64(h) + bf16_to_f64(dn))
+        if logit_rows is not None:
+            o2 = o2[list(logit_rows)]
         logits = _f32_round(matmul(o2, self.w["lm_head"]))
         return logits, argmax_lowest(logits)
 

@@ -118,12 +118,13 @@ void orc_rmsnorm(const void *x, int x_dtype, int64_t x_row_stride,
  * Matmul C = A . W^T with W stored [N, K] (one row per output feature), the
  * contraction over K of [P1] section 5.4 and [P3] "Where the reductions are":
  *     C[m,n] = sum_k A[m,k] * W[n,k]
- * Rows of C are independent of one another ([P1] section 3.3).
+ * Rows of C are independent of one another ([P1] section 3.3); every output
+ * element is its own sequential sum, so the threads share nothing.
  */
 void orc_matmul(const void *A, int a_dtype, int64_t lda, const void *W, int w_dtype,
                 int64_t ldw, double *C, int64_t ldc, int64_t M, int64_t N, int64_t K)
 {
-    #pragma omp parallel for schedule(static)
+    #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t n = 0; n < N; ++n) {
             double s = 0.0;
@@ -152,7 +153,7 @@ static const uint16_t *kv_row(const uint16_t *cache, const int32_t *table, int64
  * This is the exact result every split-KV scheme of [P1] section 5.5 and [P3]
  * "The attention detail that gets missed" reaches up to rounding, so the
  * oracle computes it unsplit.  q is [rows, Hq, D] with row stride q_row_stride
- * (elements); out is [rows, Hq, D] fp64.  Returns the maximum L seen.
+ * (elements); out is [rows, Hq, D] fp64.
  */
 void orc_decode_attn(const uint16_t *q, int64_t q_row_stride,
                      const uint16_t *k_cache, const uint16_t *v_cache,
