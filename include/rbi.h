@@ -140,17 +140,23 @@ int matmul_tuned(const void *A, int64_t lda, const void *W, int64_t ldw, void *C
  * missed").  For row r with length L = kv_lens[r] and query head h (kv head
  * g = h / (num_q_heads / num_kv_heads)):
  *     out[r,h] = sum_{j<L} softmax_j(scale * <q[r,h], k_j>) v_j
- * where k_j, v_j sit in page block_table[r][j / page_size], slot
+ * where k_j and v_j sit in page block_table[r][j / page_size], slot
  * j % page_size.  Split s covers tokens [s*split_size, min((s+1)*split_size, L));
  * the boundaries depend on nothing but L.  Per split the kernel forms a partial
  * (max m, sum l, accumulator acc) with bf16 MFMA products and fp32 softmax;
- * a second kernel combines the ceil(L / split_size) partials in ascending split
- * order (log-sum-exp rescaling) and rounds acc / l to bf16 once.
+ * a second kernel combines the ceil(L / split_size) partials with log-sum-exp
+ * rescaling in ascending split order and rounds acc / l to bf16 once.  The
+ * whole reduction tree is a function of L alone.
  *
  *  q            [rows, num_q_heads, head_dim] bf16, row stride q_row_stride
  *               (head stride head_dim)
- *  k_cache,
- *  v_cache      [num_pages, num_kv_heads, page_size, head_dim] bf16
+ *  k_cache      [num_pages, num_kv_heads, page_size, head_dim] bf16 (token-major
+ *               pages: element (t, d) of a page at t * head_dim + d)
+ *  v_cache      [num_pages, num_kv_heads, head_dim, page_size] bf16 (head-dim-major
+ *               pages: element (t, d) at d * page_size + t).  Stored this way, a
+ *               16-byte run of a V page is the 8 consecutive tokens one matrix-core
+ *               operand lane needs for the P.V product, so V is read straight into
+ *               the operand with no transposition.
  *  block_table  [rows, bt_stride] int32 physical page ids; only the first
  *               ceil(kv_lens[r] / page_size) entries of a row are read
  *  kv_lens      [rows] int32 (device), each in [1, max_kv_len]
@@ -158,9 +164,15 @@ int matmul_tuned(const void *A, int64_t lda, const void *W, int64_t ldw, void *C
  *  max_kv_len   an upper bound on every kv_lens[r]; it sizes the grid and the
  *               workspace only -- results do not depend on it
  *  workspace    >= decode_attn_workspace_size(rows, num_q_heads, head_dim,
- *               max_kv_len, split_size) bytes, 16-byte aligned
+ *               max_kv_len, split_size) bytes, 16-byte aligned.  On return it holds
+ *               the split partials: with nsmax = ceil(max_kv_len / split_size) and
+ *               item = (r * num_q_heads + h) * nsmax + s, fp32 acc[item][head_dim]
+ *               first, then fp32 (m, l)[item][2] (m in log2 units: scale *
+ *               log2(e) * <q, k>, l the sum of the bf16-rounded 2^(score - m));
+ *               splits s >= ceil(kv_lens[r] / split_size) are not written
  * Supported: head_dim 64 or 128; page_size 16; split_size a positive multiple of
- * page_size; num_q_heads % num_kv_heads == 0 with a group of 1..16 query heads;
+ * page_size, at most 1024; num_q_heads % num_kv_heads == 0 with a group of 1..16
+ * query heads;
  * q, out 16-byte aligned with row strides multiples of 8.  A kv_lens entry
  * outside [1, max_kv_len] is clamped into that range on the device (it cannot
  * be reported from there); keep lengths valid.
@@ -201,6 +213,8 @@ int decode_attn_tuned(const void *q, int64_t q_row_stride, const void *k_cache,
  *                k_row_stride / v_row_stride (head stride head_dim)
  *  slot_mapping  [tokens] int32 (device); an entry < 0 or >= num_pages*page_size
  *                is skipped (no write)
+ *  k_cache, v_cache  in the layouts decode_attn_bi documents (token-major K pages,
+ *                head-dim-major V pages)
  * Requirements: 16-byte aligned pointers, head_dim a multiple of 8, row strides
  * multiples of 8.
  */

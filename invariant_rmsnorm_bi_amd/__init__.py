@@ -236,8 +236,10 @@ def _attn_prep(q, k_cache, v_cache, block_table, kv_lens, out):
         raise RbiError("block_table and kv_lens must be int32")
     if not (k_cache.is_contiguous() and v_cache.is_contiguous() and kv_lens.is_contiguous()):
         raise RbiError("caches and kv_lens must be contiguous")
-    if k_cache.shape != v_cache.shape or k_cache.dim() != 4:
-        raise RbiError("caches must be [num_pages, num_kv_heads, page_size, head_dim]")
+    if k_cache.dim() != 4 or v_cache.shape != (k_cache.shape[0], k_cache.shape[1],
+                                               k_cache.shape[3], k_cache.shape[2]):
+        raise RbiError("caches must be K [num_pages, num_kv_heads, page_size, head_dim] and "
+                       "V [num_pages, num_kv_heads, head_dim, page_size]")
     rows, hq, d = q.shape
     if q.stride(2) != 1 or q.stride(1) != d:
         raise RbiError("q must be [rows, heads, head_dim] with packed heads")
@@ -295,7 +297,8 @@ def decode_attn_tuned(q, k_cache, v_cache, block_table, kv_lens, max_kv_len: int
 
 def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache) -> None:
     """Write k_new/v_new [tokens, Hkv, D] (or [tokens, Hkv*D] row views) into the cache
-    slots given by slot_mapping [tokens] int32 (page * page_size + offset)."""
+    slots given by slot_mapping [tokens] int32 (page * page_size + offset); K pages
+    token-major [pages, Hkv, page, D], V pages head-dim-major [pages, Hkv, D, page]."""
     _need_cuda(k_new, v_new, slot_mapping, k_cache, v_cache)
     num_pages, hkv, page, d = k_cache.shape
     tokens = k_new.shape[0]

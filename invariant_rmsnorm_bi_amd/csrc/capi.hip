@@ -73,7 +73,7 @@ int check_attn(const void *q, int64_t qs, const void *kc, const void *vc, const 
         return RBI_EINVAL;
     if (d != 64 && d != 128)
         return RBI_EUNSUPPORTED;
-    if (page != 16 || split % page)
+    if (page != 16 || split % page || split > 1024)
         return RBI_EUNSUPPORTED;
     if (hq / hkv > 16)
         return RBI_EUNSUPPORTED;
@@ -226,7 +226,7 @@ int decode_attn_tuned_split_size(int64_t rows, int num_kv_heads, int max_kv_len,
         return 16;
     const int64_t target = 2 * 256;
     int best = 16;
-    for (int S = 16; S <= 32768; S *= 2) {
+    for (int S = 16; S <= 1024; S *= 2) {
         int64_t items = 0;
         for (int64_t r = 0; r < rows; ++r) {
             int64_t L = kv_lens_host ? kv_lens_host[r] : max_kv_len;

@@ -58,9 +58,10 @@ class DecodeLayer:
         self.w = weights
         self.tuned = tuned
         self.device = device
-        shape = (num_pages, cfg.num_kv_heads, cfg.page_size, cfg.head_dim)
-        self.k_cache = torch.zeros(shape, dtype=torch.bfloat16, device=device)
-        self.v_cache = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+        self.k_cache = torch.zeros((num_pages, cfg.num_kv_heads, cfg.page_size, cfg.head_dim),
+                                   dtype=torch.bfloat16, device=device)
+        self.v_cache = torch.zeros((num_pages, cfg.num_kv_heads, cfg.head_dim, cfg.page_size),
+                                   dtype=torch.bfloat16, device=device)
 
     def _mm(self, a, w, out_dtype=torch.bfloat16):
         return (matmul_tuned if self.tuned else matmul_bi)(a, w, out_dtype=out_dtype)

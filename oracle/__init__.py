@@ -147,7 +147,8 @@ def decode_attn(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     """Unsplit decode attention (``split=None``) or the fixed-split-size
     evaluation with ascending log-sum-exp combine (``split=S``), fp64.
 
-    q: [rows, Hq, D] bf16 bits; k_cache, v_cache: [pages, Hkv, page, D] bf16 bits;
+    q: [rows, Hq, D] bf16 bits; k_cache: [pages, Hkv, page, D] bf16 bits (token-major
+    pages); v_cache: [pages, Hkv, D, page] bf16 bits (head-dim-major pages);
     block_table: [rows, max_pages] int32; kv_lens: [rows] int32 (each >= 1).
     Returns [rows, Hq, D] float64.
     """
@@ -159,6 +160,7 @@ def decode_attn(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     rows, hq, d = q.shape
     _, hkv, page, d2 = kc.shape
     assert d == d2 and hq % hkv == 0 and lens.shape == (rows,)
+    assert vc.shape == (kc.shape[0], hkv, d, page)
     assert (lens >= 1).all()
     out = np.empty((rows, hq, d), dtype=np.float64)
     args = (_ptr(q), hq * d, _ptr(kc), _ptr(vc), _ptr(bt), bt.shape[1], _ptr(lens), _ptr(out),

@@ -57,9 +57,10 @@ class DenseLayerOracle:
     def __init__(self, dims: LayerDims, weights: dict, num_pages: int):
         self.d = dims
         self.w = {k: np.ascontiguousarray(v).view(np.uint16) for k, v in weights.items()}
-        shape = (num_pages, dims.num_kv_heads, dims.page_size, dims.head_dim)
-        self.k_cache = np.zeros(shape, dtype=np.uint16)
-        self.v_cache = np.zeros(shape, dtype=np.uint16)
+        self.k_cache = np.zeros((num_pages, dims.num_kv_heads, dims.page_size, dims.head_dim),
+                                dtype=np.uint16)
+        self.v_cache = np.zeros((num_pages, dims.num_kv_heads, dims.head_dim, dims.page_size),
+                                dtype=np.uint16)
 
     def step(self, tokens, block_tables: np.ndarray, positions,
              logit_rows=None) -> tuple[np.ndarray, np.ndarray]:
@@ -82,7 +83,7 @@ class DenseLayerOracle:
             p = int(positions[b])
             page = int(bt[b, p // d.page_size])
             self.k_cache[page, :, p % d.page_size, :] = k[b]
-            self.v_cache[page, :, p % d.page_size, :] = v[b]
+            self.v_cache[page, :, :, p % d.page_size] = v[b]
         lens = (positions + 1).astype(np.int32)
         o = decode_attn(np.ascontiguousarray(q), self.k_cache, self.v_cache, bt, lens,
                         1.0 / np.sqrt(hd))

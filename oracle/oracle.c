@@ -137,12 +137,21 @@ void orc_matmul(const void *A, int a_dtype, int64_t lda, const void *W, int w_dt
 
 /* Logical token j of request r, kv head g, through the block table: the page
  * is table[r][j / page], the slot j % page ([P1] section 5.5: the KV cache and
- * page table are the arrangement attention reduces over). */
-static const uint16_t *kv_row(const uint16_t *cache, const int32_t *table, int64_t bt_stride,
-                              int64_t r, int64_t j, int g, int hkv, int page, int d)
+ * page table are the arrangement attention reduces over).  K pages are stored
+ * token-major, [page][kv head][slot][d]; V pages head-dim-major,
+ * [page][kv head][d][slot] (the documented cache layouts). */
+static const uint16_t *k_row(const uint16_t *cache, const int32_t *table, int64_t bt_stride,
+                             int64_t r, int64_t j, int g, int hkv, int page, int d)
 {
     int64_t phys = table[r * bt_stride + j / page];
     return cache + ((phys * hkv + g) * (int64_t)page + j % page) * (int64_t)d;
+}
+
+static double v_elem(const uint16_t *cache, const int32_t *table, int64_t bt_stride,
+                     int64_t r, int64_t j, int g, int hkv, int page, int d, int i)
+{
+    int64_t phys = table[r * bt_stride + j / page];
+    return widen_bf16(cache[((phys * hkv + g) * (int64_t)d + i) * (int64_t)page + j % page]);
 }
 
 /*
@@ -170,7 +179,7 @@ void orc_decode_attn(const uint16_t *q, int64_t q_row_stride,
             double *s = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
             double m = -INFINITY;
             for (int64_t j = 0; j < L; ++j) {
-                const uint16_t *kj = kv_row(k_cache, block_table, bt_stride, r, j, g, hkv, page, d);
+                const uint16_t *kj = k_row(k_cache, block_table, bt_stride, r, j, g, hkv, page, d);
                 double dot = 0.0;
                 for (int i = 0; i < d; ++i)
                     dot += widen_bf16(qh[i]) * widen_bf16(kj[i]);
@@ -187,10 +196,9 @@ void orc_decode_attn(const uint16_t *q, int64_t q_row_stride,
             for (int i = 0; i < d; ++i)
                 o[i] = 0.0;
             for (int64_t j = 0; j < L; ++j) {
-                const uint16_t *vj = kv_row(v_cache, block_table, bt_stride, r, j, g, hkv, page, d);
                 double p = s[j] / l;
                 for (int i = 0; i < d; ++i)
-                    o[i] += p * widen_bf16(vj[i]);
+                    o[i] += p * v_elem(v_cache, block_table, bt_stride, r, j, g, hkv, page, d, i);
             }
             free(s);
         }
@@ -243,7 +251,7 @@ void orc_decode_attn_split(const uint16_t *q, int64_t q_row_stride,
                 int64_t j0 = sidx * split, j1 = j0 + split < L ? j0 + split : L;
                 double m = -INFINITY;
                 for (int64_t j = j0; j < j1; ++j) {
-                    const uint16_t *kj = kv_row(k_cache, block_table, bt_stride, r, j, g, hkv, page, d);
+                    const uint16_t *kj = k_row(k_cache, block_table, bt_stride, r, j, g, hkv, page, d);
                     double dot = 0.0;
                     for (int i = 0; i < d; ++i)
                         dot += widen_bf16(qh[i]) * widen_bf16(kj[i]);
@@ -252,15 +260,15 @@ void orc_decode_attn_split(const uint16_t *q, int64_t q_row_stride,
                 }
                 double l = 0.0;
                 for (int64_t j = j0; j < j1; ++j) {
-                    const uint16_t *kj = kv_row(k_cache, block_table, bt_stride, r, j, g, hkv, page, d);
-                    const uint16_t *vj = kv_row(v_cache, block_table, bt_stride, r, j, g, hkv, page, d);
+                    const uint16_t *kj = k_row(k_cache, block_table, bt_stride, r, j, g, hkv, page, d);
                     double dot = 0.0;
                     for (int i = 0; i < d; ++i)
                         dot += widen_bf16(qh[i]) * widen_bf16(kj[i]);
                     double p = exp(scale * dot - m);
                     l += p;
                     for (int i = 0; i < d; ++i)
-                        acc[sidx * d + i] += p * widen_bf16(vj[i]);
+                        acc[sidx * d + i] += p * v_elem(v_cache, block_table, bt_stride, r, j, g,
+                                                        hkv, page, d, i);
                 }
                 ms[sidx] = m;
                 ls[sidx] = l;

@@ -97,7 +97,8 @@ def linspace_matrix(rows: int, cols: int, lo: float = -1000.0, hi: float = 1000.
 class PagedKV:
     """A paged KV cache plus per-request block tables.
 
-    k_cache, v_cache: [num_pages, Hkv, page_size, D] bf16
+    k_cache: [num_pages, Hkv, page_size, D] bf16 (token-major pages)
+    v_cache: [num_pages, Hkv, D, page_size] bf16 (head-dim-major pages)
     block_table:      [num_reqs, max_pages] int32, physical page ids (seeded permutation)
     kv_lens:          [num_reqs] int32, every entry >= 1
     """
@@ -147,9 +148,8 @@ def paged_kv(kv_lens, num_kv_heads: int, head_dim: int, page_size: int, *,
     for r, n in enumerate(need):
         bt[r, :n] = perm[pos:pos + n]
         pos += n
-    shape = (total, num_kv_heads, page_size, head_dim)
-    k = normal(shape, seed=seed, device=device)
-    v = normal(shape, seed=seed + 1, device=device)
+    k = normal((total, num_kv_heads, page_size, head_dim), seed=seed, device=device)
+    v = normal((total, num_kv_heads, head_dim, page_size), seed=seed + 1, device=device)
     if stale_fill is not None:
         k[poison] = stale_fill
         v[poison] = stale_fill
@@ -158,7 +158,7 @@ def paged_kv(kv_lens, num_kv_heads: int, head_dim: int, page_size: int, *,
             off = l - (need[r] - 1) * page_size
             if off < page_size:
                 k[last, :, off:, :] = stale_fill
-                v[last, :, off:, :] = stale_fill
+                v[last, :, :, off:] = stale_fill
     return PagedKV(k_cache=k, v_cache=v, block_table=bt.to(device),
                    kv_lens=torch.tensor(lens, dtype=torch.int32, device=device),
                    page_size=page_size, num_kv_heads=num_kv_heads, head_dim=head_dim,

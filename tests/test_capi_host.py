@@ -99,6 +99,7 @@ def test_decode_attn_validation():
     assert _attn(d=96) == EUNSUPPORTED
     assert _attn(page=32) == EUNSUPPORTED
     assert _attn(split=250) == EUNSUPPORTED        # not a multiple of the page
+    assert _attn(split=2048) == EUNSUPPORTED       # longer than 1024 tokens
     assert _attn(hq=64, hkv=2) == EUNSUPPORTED      # group of 32 query heads
     assert _attn(hq=63) == EINVAL                   # not a multiple of hkv
     assert _attn(maxlen=0) == EINVAL
@@ -109,7 +110,7 @@ def test_decode_attn_validation():
     assert _attn(qs=64 * 128 - 8) == EINVAL
     assert _attn(ws=NULL) == EWORKSPACE
     need = rbi.decode_attn_workspace_size(4, 64, 128, 32768, 256)
-    assert need == 4 * 64 * 128 * 130 * 4
+    assert need == 4 * 64 * 128 * 130 * 4     # 128 splits of 256
     assert _attn(wsb=need - 1) == EWORKSPACE
 
 
@@ -117,13 +118,14 @@ def test_decode_attn_workspace_depends_only_on_bounds():
     a = rbi.decode_attn_workspace_size(256, 64, 128, 32768, 256)
     assert a == 256 * 64 * 128 * (128 + 2) * 4
     assert rbi.decode_attn_workspace_size(5, 4, 64, 63, 16) == 5 * 4 * 4 * 66 * 4
+    assert rbi.decode_attn_workspace_size(5, 4, 64, 65, 16) == 5 * 4 * 5 * 66 * 4
 
 
 def test_tuned_split_size_follows_the_batch():
     # balanced scheduling: long single request -> small splits; big batch -> large
     one = rbi.decode_attn_tuned_split_size(1, 4, 32768, [32768])
     many = rbi.decode_attn_tuned_split_size(256, 4, 32768, [32768] * 256)
-    assert one <= 256 and many >= 4096
+    assert one <= 256 and many == 1024
     assert one % 16 == 0 and many % 16 == 0
     # the fixed-size kernel would use 256 in both cases
 

@@ -34,9 +34,16 @@ def _oracle(q, kv, scale, rows=None):
 
 
 def _tol_ok(out, ref):
-    err = np.abs(out.double().cpu().numpy() - ref).max()
-    rms = np.sqrt(np.mean(ref ** 2))
-    return err <= 2e-2 * rms, err, rms
+    """max|out - ref| <= 2e-2 * RMS(ref), per row: each row is its own attention
+    problem, and a batch-wide RMS would let the small outputs of long rows set the
+    bar for the larger outputs of short ones.  Returns (ok, worst ratio, its row)."""
+    o = out.double().cpu().numpy().reshape(ref.shape[0], -1)
+    r = ref.reshape(ref.shape[0], -1)
+    err = np.abs(o - r).max(1)
+    rms = np.sqrt(np.mean(r ** 2, 1))
+    ratio = err / rms
+    worst = int(np.argmax(ratio))
+    return bool((ratio <= 2e-2).all()), float(ratio[worst]), worst
 
 
 def _run(fn, q, kv, max_len, **kw):
@@ -50,8 +57,8 @@ def test_c1_tiny_parity_and_rows_bitwise():
     q = synth.normal((3, 4, 64), seed=100).to(DEV)
     scale = 1 / 8
     out = _run(rbi.decode_attn_bi, q, kv, 63, split_size=16, scale=scale)
-    ok, err, rms = _tol_ok(out, _oracle(q, kv, scale))
-    assert ok, (err, rms)
+    ok, ratio, row = _tol_ok(out, _oracle(q, kv, scale))
+    assert ok, (ratio, row)
     assert not torch.isnan(out.float()).any()
     for r in range(3):
         sub = synth.PagedKV(kv.k_cache, kv.v_cache, kv.block_table[r:r + 1].contiguous(),
@@ -76,8 +83,8 @@ def test_c4_heads_parity(lens):
     ref = _oracle(q, kv, scale)
     for fn, kw in ((rbi.decode_attn_bi, dict(split_size=256)), (rbi.decode_attn_tuned, {})):
         out = _run(fn, q, kv, max(lens), scale=scale, **kw)
-        ok, err, rms = _tol_ok(out, ref)
-        assert ok, (fn.__name__, err, rms)
+        ok, ratio, row = _tol_ok(out, ref)
+        assert ok, (fn.__name__, ratio, row)
 
 
 def test_single_token_is_exact():
@@ -87,7 +94,7 @@ def test_single_token_is_exact():
     out = _run(rbi.decode_attn_bi, q, kv, 1)
     for r in range(3):
         p = int(kv.block_table[r, 0])
-        v0 = kv.v_cache[p, :, 0, :]                       # [4, 128]
+        v0 = kv.v_cache[p, :, :, 0]                       # [4, 128]
         assert torch.equal(out[r], v0.repeat_interleave(16, 0))
 
 
@@ -99,8 +106,8 @@ def test_c4_full_batch_sampled_parity_and_batch_invariance():
     scale = 1 / math.sqrt(128)
     out = _run(rbi.decode_attn_bi, q, kv, 32768)
     rows = [0, 17, 100, 255]
-    ok, err, rms = _tol_ok(out[rows], _oracle(q, kv, scale, rows=rows))
-    assert ok, (err, rms)
+    ok, ratio, row = _tol_ok(out[rows], _oracle(q, kv, scale, rows=rows))
+    assert ok, (ratio, row)
     # every row alone and in random sub-batches gives the same bits
     rng = np.random.default_rng(synth.SEED_BATCH)
     for B in (1, 2, 3, 7, 16, 64, 255):
@@ -133,13 +140,13 @@ def test_grid_extent_and_page_placement_do_not_matter():
 
 
 def test_kv_growth_across_split_boundaries():
-    # one request grows by one token per step from 240 to 1040 tokens, crossing the
-    # 256/512/768/1024 boundaries; at every length its output in a random batch equals
-    # its output alone, and the partials of completed splits never change
-    D, HKV, HQ, S = 128, 4, 64, 256
-    pool_lens = synth.uniform_lengths(32, 1, 4096, seed=77)
+    # one request grows by one token per step from 240 to 2100 tokens, crossing the
+    # split boundaries 256, 512, ..., 2048; at every length its output in a random
+    # batch equals its output alone, and the partials of completed splits never change
+    D, HKV, HQ, S, LMAX = 128, 4, 64, 256, 4096
+    pool_lens = synth.uniform_lengths(32, 1, LMAX, seed=77)
     others = synth.paged_kv(pool_lens, HKV, D, 16, seed=7)
-    probe = synth.paged_kv([1040], HKV, D, 16, seed=8, page_seed=9)
+    probe = synth.paged_kv([2100], HKV, D, 16, seed=8, page_seed=9)
     q = synth.normal((1, HQ, D), seed=10).to(DEV)
     qo = synth.normal((32, HQ, D), seed=11).to(DEV)
     # one cache holding both: probe pages appended after the others'
@@ -147,26 +154,26 @@ def test_kv_growth_across_split_boundaries():
     kc = torch.cat([others.k_cache, probe.k_cache]).to(DEV)
     vc = torch.cat([others.v_cache, probe.v_cache]).to(DEV)
     bt_p = probe.block_table + n_o
-    maxp = 4096 // 16
+    maxp = LMAX // 16
     bt_o = torch.full((32, maxp), int(others.extra["poison_page"]), dtype=torch.int32)
     bt_o[:, : others.block_table.shape[1]] = others.block_table
     bt_pp = torch.full((1, maxp), n_o + int(probe.extra["poison_page"]), dtype=torch.int32)
     bt_pp[:, : bt_p.shape[1]] = bt_p
+    bt_pp_d = bt_pp.to(DEV)
     rng = np.random.default_rng(12)
-    done_partials = {}
-    for L in range(240, 1041):
+    nsmax = -(-LMAX // S)
+    ws1 = torch.zeros(rbi.decode_attn_workspace_size(1, HQ, D, LMAX, S), dtype=torch.uint8,
+                      device=DEV)
+    done = {}
+    for L in range(240, 2101):
         lens1 = torch.tensor([L], dtype=torch.int32, device=DEV)
-        ws1 = torch.zeros(rbi.decode_attn_workspace_size(1, HQ, D, 4096, S), dtype=torch.uint8,
-                          device=DEV)
-        alone = rbi.decode_attn_bi(q, kc, vc, bt_pp.to(DEV), lens1, 4096, S, workspace=ws1)
-        # partials of splits that ended before L: bit-identical at every later length
-        nsmax = 4096 // S
+        alone = rbi.decode_attn_bi(q, kc, vc, bt_pp_d, lens1, LMAX, S, workspace=ws1)
         acc = ws1[: HQ * nsmax * D * 4].view(torch.float32).view(HQ, nsmax, D)
-        for s in range(L // S):
-            if s in done_partials:
-                assert torch.equal(acc[:, s], done_partials[s]), (L, s)
+        for k in range(L // S):
+            if k in done:
+                assert torch.equal(acc[:, k], done[k]), (L, k)
             else:
-                done_partials[s] = acc[:, s].clone()
+                done[k] = acc[:, k].clone()
         B = int(rng.integers(2, 33))
         pos = int(rng.integers(0, B))
         mem = rng.choice(32, size=B - 1, replace=False)
@@ -174,8 +181,9 @@ def test_kv_growth_across_split_boundaries():
         btb = torch.cat([bt_o[mem[:pos]], bt_pp, bt_o[mem[pos:]]]).to(DEV)
         lb = torch.tensor([pool_lens[i] for i in mem[:pos]] + [L] +
                           [pool_lens[i] for i in mem[pos:]], dtype=torch.int32, device=DEV)
-        ob = rbi.decode_attn_bi(qb, kc, vc, btb, lb, 4096, S)
+        ob = rbi.decode_attn_bi(qb, kc, vc, btb, lb, LMAX, S)
         assert torch.equal(ob[pos], alone[0]), L
+    assert sorted(done) == list(range(8))
 
 
 def test_chunked_prefill_equals_unchunked():
@@ -193,7 +201,7 @@ def test_chunked_prefill_equals_unchunked():
 
     def fresh():
         return (torch.full((npages + 8, HKV, 16, D), float("nan"), dtype=torch.bfloat16, device=DEV),
-                torch.full((npages + 8, HKV, 16, D), float("nan"), dtype=torch.bfloat16, device=DEV))
+                torch.full((npages + 8, HKV, D, 16), float("nan"), dtype=torch.bfloat16, device=DEV))
 
     kc, vc = fresh()
     rbi.kv_append(k_new, v_new, slots, kc, vc)
@@ -215,7 +223,7 @@ def test_chunked_prefill_equals_unchunked():
 def test_kv_append_exact_placement():
     T, HKV, D = 37, 4, 128
     kc = torch.zeros((20, HKV, 16, D), dtype=torch.bfloat16, device=DEV)
-    vc = torch.zeros_like(kc)
+    vc = torch.zeros((20, HKV, D, 16), dtype=torch.bfloat16, device=DEV)
     k_new = synth.normal((T, HKV * D), seed=18).to(DEV)
     v_new = synth.normal((T, HKV * D), seed=19).to(DEV)
     slots = torch.randperm(20 * 16, generator=synth.gen(20))[:T].to(torch.int32)
@@ -229,10 +237,12 @@ def test_kv_append_exact_placement():
         s = int(slots[t])
         if 0 <= s < 320:
             assert torch.equal(kc_h[s // 16, :, s % 16], kn[t])
-            assert torch.equal(vc_h[s // 16, :, s % 16], vn[t])
+            assert torch.equal(vc_h[s // 16, :, :, s % 16], vn[t])
             written[s] = True
     flat = kc_h.permute(0, 2, 1, 3).reshape(320, -1)
     assert float(flat[~written].abs().max()) == 0
+    vflat = vc_h.permute(0, 3, 1, 2).reshape(320, -1)
+    assert float(vflat[~written].abs().max()) == 0
 
 
 def test_tuned_twin_sensitivity():

@@ -99,9 +99,8 @@ def test_probe_tokens_and_logits_independent_of_batch(weights):
     total = sum(need) + probe_pages + 1
     perm = synth.page_ids(total, seed=synth.SEED_PAGES).numpy()
     layer = DecodeLayer(CFG, weights, num_pages=total)
-    shape = layer.k_cache.shape
-    layer.k_cache.copy_(synth.normal(shape, seed=60, device=DEV))
-    layer.v_cache.copy_(synth.normal(shape, seed=61, device=DEV))
+    layer.k_cache.copy_(synth.normal(layer.k_cache.shape, seed=60, device=DEV))
+    layer.v_cache.copy_(synth.normal(layer.v_cache.shape, seed=61, device=DEV))
     off = 0
     tables = []
     for n in need:

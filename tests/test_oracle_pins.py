@@ -258,7 +258,7 @@ def _gather(kv, r):
     for j in range(L):
         p = int(kv.block_table[r, j // pg])
         ks.append(kv.k_cache[p, :, j % pg, :])
-        vs.append(kv.v_cache[p, :, j % pg, :])
+        vs.append(kv.v_cache[p, :, :, j % pg])
     return torch.stack(ks).double(), torch.stack(vs).double()
 
 
@@ -309,8 +309,8 @@ def test_decode_attn_two_token_closed_form():
     p = int(kv.block_table[0, 0])
     kv.k_cache[p, 0, 0] = torch.tensor([1.0, 0, 0, 0])
     kv.k_cache[p, 0, 1] = torch.tensor([0, 1.0, 0, 0])
-    kv.v_cache[p, 0, 0] = torch.tensor([1.0, 0, 0, 0])
-    kv.v_cache[p, 0, 1] = torch.tensor([0, 1.0, 0, 0])
+    kv.v_cache[p, 0, :, 0] = torch.tensor([1.0, 0, 0, 0])
+    kv.v_cache[p, 0, :, 1] = torch.tensor([0, 1.0, 0, 0])
     q = torch.tensor([[[2.0, -1.0, 0, 0]]]).to(torch.bfloat16)
     scale = 0.5
     got = _attn(q, kv, scale)[0, 0]
@@ -341,7 +341,7 @@ def test_decode_attn_block_table_indexing():
     pg = kv.page_size
     for r, L in enumerate(lens):
         for j in range(L):
-            kv.v_cache[int(kv.block_table[r, j // pg]), 0, j % pg, 0] = float(j)
+            kv.v_cache[int(kv.block_table[r, j // pg]), 0, 0, j % pg] = float(j)
     got = _attn(synth.normal((len(lens), 1, 4), seed=2), kv, 1.0)
     for r, L in enumerate(lens):
         assert abs(got[r, 0, 0] - (L - 1) / 2.0) < 1e-12
