@@ -11,6 +11,10 @@ Compiles every csrc/*.hip with hipcc in parallel and links them into
                                source spells out
   -target-feature -packed-fp32-ops
                                keep the compiler from forming packed fp32 VALU ops
+  -amdgpu-mfma-vgpr-form       keep MFMA accumulators in ordinary VGPRs; with the
+                               accumulation-register form the register allocator
+                               rotates loop-carried accumulators through copies
+                               (three extra moves per MFMA in the matmul main loop)
 """
 from __future__ import annotations
 
@@ -31,6 +35,7 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument", f"-I{INCLUDE}",
 ]
 

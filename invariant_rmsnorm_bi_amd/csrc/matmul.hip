@@ -27,6 +27,28 @@ namespace {
 
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int GROUP_M = 8;
+constexpr int BIG_GROUP_M = 4;
+constexpr int NUM_XCD = 8;
+
+// Output tile of workgroup `pid`.  Workgroups are dealt to the eight XCDs (each with
+// its own L2) round robin, so pid -> XCD is pid % 8; first give each XCD a contiguous
+// run of logical tile ids, then order tiles in groups of `group_m` tile rows that
+// sweep the columns together.  The workgroups resident on one XCD then cover a compact
+// block of C and share their A rows and W rows in that XCD's L2.  The map is a
+// bijection on [0, tiles_m * tiles_n) whatever the placement; only speed depends on it.
+__device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int group_m,
+                                            int &tm, int &tn)
+{
+    const int total = tiles_m * tiles_n;
+    const int per = total / NUM_XCD, extra = total % NUM_XCD;
+    const int xcd = pid % NUM_XCD, local = pid / NUM_XCD;
+    const int t = xcd * per + min(xcd, extra) + local;
+    const int in_group = group_m * tiles_n;
+    const int first_m = (t / in_group) * group_m;
+    const int gsz = min(tiles_m - first_m, group_m);
+    tm = first_m + (t % in_group) % gsz;
+    tn = (t % in_group) / gsz;
+}
 
 // LDS tile [rows][BK] bf16; 16-byte chunk q of row r lives at chunk slot q ^ (r & 7)
 // so that the 16 rows read by one MFMA fragment spread over the banks.
@@ -49,13 +71,8 @@ __global__ __launch_bounds__(256, 2) void mm_tile_kernel(
     W += kb0;
     const int Kl = (int)((K - kb0) < k_split ? (K - kb0) : k_split);
 
-    // grouped tile order: GROUP_M row-tiles share each column sweep (L2 reuse of W)
-    const int pid = blockIdx.x;
-    const int in_group = GROUP_M * tiles_n;
-    const int first_m = (pid / in_group) * GROUP_M;
-    const int gsz = min(tiles_m - first_m, GROUP_M);
-    const int tm = first_m + (pid % in_group) % gsz;
-    const int tn = (pid % in_group) / gsz;
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, GROUP_M, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -150,7 +167,222 @@ __global__ __launch_bounds__(256, 2) void mm_tile_kernel(
     }
 }
 
-// C[m, n..n+3] = sum over splits (ascending) of ws[split][m][n..n+3]
+// Pipelined large-tile kernel for K a multiple of 32: a TBM x TBN output tile per
+// workgroup of 2*WN waves in a 2 x WN grid, each wave owning (TBM/2) batch rows x
+// (TBN/WN) features.  K advances one MFMA step (32 k) per stage; P stages of
+// operand tiles are in flight at once, copied from global memory straight into LDS
+// (global_load_lds_dwordx4: no register staging), so a load has P-1 stages of MFMA
+// work to arrive in.  Operand fragments are double buffered in registers: the next
+// stage's are read from LDS while this stage's MFMAs run.  The MFMA instruction, its
+// operand roles, the k fragment mapping and the ascending k order are those of
+// mm_tile_kernel, so each element gets the same bits from either kernel (a K that is
+// 32 mod 64 only drops the tile kernel's trailing all-zero step, an exact no-op).
+//
+// LDS stage layout: TBM activation rows then TBN weight rows, each 32 k (64 bytes,
+// four 16-byte chunks); chunk c of stage row r sits in slot c ^ pswz(r).  One load
+// instruction fills 16 consecutive rows (lane l -> row l/4, slot l%4) and each lane
+// fetches the global chunk that belongs in its slot.  A fragment read (16 consecutive
+// rows, one chunk) then touches 16 distinct bank groups: conflict free whether the
+// LDS serves 8 or 16 lanes of a 16-byte read per cycle.
+constexpr int PK = 32;
+
+__device__ __forceinline__ int pswz(int r)
+{
+    return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+// Wait until at most N of this wave's global loads are outstanding and all of its LDS
+// reads have returned, then meet the other waves.  s_waitcnt immediate (gfx9):
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].  The empty asm
+// statements keep the compiler from moving memory accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int TBM, int TBN, int WN, int P, bool OUT_BF16>
+__global__ __launch_bounds__(128 * WN, 1) void mm_pipe_kernel(
+    const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restrict__ W, int64_t ldw,
+    void *__restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n)
+{
+    constexpr int NW = 2 * WN;                   // waves
+    constexpr int WTM = TBM / 2, WTN = TBN / WN; // wave tile
+    constexpr int FM = WTM / 16, FN = WTN / 16;  // MFMA blocks per wave
+    constexpr int ROWS = TBM + TBN;
+    constexpr int STAGE = ROWS * PK;             // bf16 elements per stage
+    constexpr int LPW = ROWS / (16 * NW);        // 16-row load instructions per wave per stage
+    static_assert(ROWS % (16 * NW) == 0 && TBM % (16 * NW) == 0 && WTN % 16 == 0 &&
+                      WTM % 16 == 0, "tile shape");
+    static_assert(P >= 3, "pipeline depth");
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, BIG_GROUP_M, tm, tn);
+    const int m0 = tm * TBM, n0 = tn * TBN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int lr = lane & 15, lq = lane >> 4;
+
+    // source of this lane's 16 bytes in load instruction i of a stage (k = 0); rows
+    // past M or N read a valid row whose results are never stored
+    const uint16_t *src[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int R = (i * NW + wave) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ pswz(R);
+        if ((i * NW + wave) * 16 < TBM)
+            src[i] = A + (int64_t)min(m0 + R, M - 1) * lda + 8 * c;
+        else
+            src[i] = W + (int64_t)min(n0 + R - TBM, N - 1) * ldw + 8 * c;
+    }
+    auto issue = [&](int stage, int buf) {
+        uint16_t *base = smem_dyn + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < LPW; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(src[i] + stage * PK),
+                (void __attribute__((address_space(3))) *)(base + (i * NW + wave) * 16 * PK), 16,
+                0, 0);
+    };
+    auto read_frags = [&](int buf, bf16x8_t (&fa)[FM], bf16x8_t (&fw)[FN]) {
+        const uint16_t *base = smem_dyn + buf * STAGE;
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            const int R = TBM + wn * WTN + b * 16 + lr;
+            fw[b] = as_bf16x8(*reinterpret_cast<const uint4 *>(base + R * PK + 8 * (lq ^ pswz(R))));
+        }
+#pragma unroll
+        for (int b = 0; b < FM; ++b) {
+            const int R = wm * WTM + b * 16 + lr;
+            fa[b] = as_bf16x8(*reinterpret_cast<const uint4 *>(base + R * PK + 8 * (lq ^ pswz(R))));
+        }
+    };
+
+    f32x4_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto mfmas = [&](const bf16x8_t (&fa)[FM], const bf16x8_t (&fw)[FN]) {
+#pragma unroll
+        for (int bm = 0; bm < FM; ++bm)
+#pragma unroll
+            for (int bn = 0; bn < FN; ++bn)
+                acc[bm][bn] = mfma_16x16x32_bf16(fw[bn], fa[bm], acc[bm][bn]);
+    };
+
+    const int nk = K / PK;
+    // stage s lives in buffer s % P; stages 0 .. P-1 are issued up front and stage
+    // s + P is issued once every wave has read stage s's fragments.  Before step kt
+    // waits, stages 0 .. kt+P-1 have been issued (loads complete in issue order).
+#pragma unroll
+    for (int st = 0; st < P; ++st)
+        if (st < nk)
+            issue(st, st);
+    if (nk >= P)
+        wait_loads_and_barrier<(P - 1) * LPW>();
+    else
+        wait_loads_and_barrier<0>();
+    bf16x8_t fa0[FM], fw0[FN], fa1[FM], fw1[FN];
+    read_frags(0, fa0, fw0);
+
+    // one k step: make stage kt+1 resident, refill the buffer stage kt vacated, read
+    // stage kt+1's fragments, run stage kt's MFMAs.  The steady-state step is branch
+    // free so that its LDS reads can be interleaved with its MFMAs, which hides LDS
+    // latency under matrix work (instruction classes: 0x8 MFMA, 0x100 LDS read).
+    auto steady = [&](int kt, const bf16x8_t (&fa)[FM], const bf16x8_t (&fw)[FN],
+                      bf16x8_t (&na)[FM], bf16x8_t (&nw)[FN]) {
+        wait_loads_and_barrier<(P - 2) * LPW>();
+        issue(kt + P, kt % P);
+        read_frags((kt + 1) % P, na, nw);
+        mfmas(fa, fw);
+        constexpr int NR = FM + FN, MPR = FM * FN / NR;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - NR * MPR, 0);
+    };
+    // the last P steps: fewer stages left to issue and to wait for
+    auto drain = [&](int kt, const bf16x8_t (&fa)[FM], const bf16x8_t (&fw)[FN],
+                     bf16x8_t (&na)[FM], bf16x8_t (&nw)[FN]) {
+        if (kt + 1 < nk) {
+            if (kt + P - 1 < nk)
+                wait_loads_and_barrier<(P - 2) * LPW>();
+            else
+                wait_loads_and_barrier<0>();
+            if (kt + P < nk)
+                issue(kt + P, kt % P);
+            read_frags((kt + 1) % P, na, nw);
+        }
+        mfmas(fa, fw);
+    };
+    int kt = 0;
+    for (; kt + P + 1 < nk; kt += 2) {
+        steady(kt, fa0, fw0, fa1, fw1);
+        steady(kt + 1, fa1, fw1, fa0, fw0);
+    }
+    for (; kt + 1 < nk; kt += 2) {
+        drain(kt, fa0, fw0, fa1, fw1);
+        drain(kt + 1, fa1, fw1, fa0, fw0);
+    }
+    if (kt < nk)
+        drain(kt, fa0, fw0, fa1, fw1);
+
+    // lane holds batch row m = lane % 16 of each block and features n = 4*(lane/16) + j
+#pragma unroll
+    for (int bm = 0; bm < FM; ++bm) {
+        const int m = m0 + wm * WTM + bm * 16 + lr;
+        if (m >= M)
+            continue;
+#pragma unroll
+        for (int bn = 0; bn < FN; ++bn) {
+            const int n = n0 + wn * WTN + bn * 16 + 4 * lq;
+            if (n >= N)
+                continue;
+            const f32x4_t v = acc[bm][bn];
+            if constexpr (OUT_BF16) {
+                uint2 o;
+                o.x = pack_bf16x2(v[0], v[1]);
+                o.y = pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(C) + (int64_t)m * ldc + n) = o;
+            } else {
+                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(C) + (int64_t)m * ldc + n) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+    }
+}
+
+template <int TBM, int TBN, int WN, int P>
+hipError_t launch_pipe(const MatmulArgs &a, hipStream_t s)
+{
+    const int tiles_m = (int)((a.M + TBM - 1) / TBM), tiles_n = (int)((a.N + TBN - 1) / TBN);
+    const size_t lds = (size_t)P * (TBM + TBN) * PK * sizeof(uint16_t);
+    const void *fn = a.c_bf16 ? (const void *)mm_pipe_kernel<TBM, TBN, WN, P, true>
+                              : (const void *)mm_pipe_kernel<TBM, TBN, WN, P, false>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess)
+        return e;
+    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(128 * WN);
+    if (a.c_bf16)
+        mm_pipe_kernel<TBM, TBN, WN, P, true><<<grid, block, lds, s>>>(
+            a.A, a.lda, a.W, a.ldw, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_m, tiles_n);
+    else
+        mm_pipe_kernel<TBM, TBN, WN, P, false><<<grid, block, lds, s>>>(
+            a.A, a.lda, a.W, a.ldw, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ ws, int splits,
                                                             int64_t M, int64_t N, void *C,
@@ -200,6 +432,39 @@ hipError_t launch_tiles(const MatmulArgs &a, int splits, int64_t k_split, void *
 
 hipError_t launch_matmul_bi(const MatmulArgs &a, hipStream_t s)
 {
+    // The tile shape is picked from the problem size; that changes which wave
+    // computes an element, never the element's arithmetic.  Each candidate is
+    // priced as (rounds of 256 workgroups) x (tile area) / (throughput per unit area
+    // measured for that tile on MI355X): big tiles are efficient once there are
+    // enough of them, small tiles keep all 256 compute units streaming weights when
+    // M is small.
+    if (a.K % PK == 0) {
+        struct Cand {
+            int tbm, tbn;
+            double eff;
+        };
+        static constexpr Cand cands[] = {{256, 256, 0.56}, {256, 128, 0.42}, {128, 128, 0.39},
+                                         {128, 64, 0.20},  {64, 64, 0.15},   {64, 32, 0.10}};
+        int best = 0;
+        double best_cost = 0;
+        for (int i = 0; i < 6; ++i) {
+            const Cand &c = cands[i];
+            const int64_t tiles = ((a.M + c.tbm - 1) / c.tbm) * ((a.N + c.tbn - 1) / c.tbn);
+            const double cost = (double)((tiles + 255) / 256) * c.tbm * c.tbn / c.eff;
+            if (i == 0 || cost < best_cost) {
+                best = i;
+                best_cost = cost;
+            }
+        }
+        switch (best) {
+        case 0: return launch_pipe<256, 256, 4, 4>(a, s);
+        case 1: return launch_pipe<256, 128, 2, 6>(a, s);
+        case 2: return launch_pipe<128, 128, 2, 8>(a, s);
+        case 3: return launch_pipe<128, 64, 2, 12>(a, s);
+        case 4: return launch_pipe<64, 64, 2, 8>(a, s);
+        default: return launch_pipe<64, 32, 1, 16>(a, s);
+        }
+    }
     return launch_tiles(a, 1, a.K, a.C, a.ldc, a.c_bf16, 0, s);
 }
 

@@ -39,7 +39,8 @@ def test_c1_parity_and_rows_bitwise_across_batch():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 512, 256), (17, 4096, 4096), (130, 260, 1032),
-                                   (257, 9216, 512), (64, 128, 8)])
+                                   (257, 9216, 512), (64, 128, 8), (300, 260, 576),
+                                   (600, 1004, 128)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_integer_inputs_exact(M, N, K, out_dtype):
     # integers in [-4, 4]: every partial sum is an integer below 2^24, so fp32 is exact
