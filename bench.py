@@ -202,25 +202,28 @@ def twin_points(wl: Workload):
 # CPU oracle baseline (bounded sample of the same workload)
 # --------------------------------------------------------------------------------------
 
+CPU_RMS_ROWS, CPU_MM_ROWS, CPU_ATT_ROWS = 2048, 96, 48
+
+
 def cpu_baseline(wl: Workload, step_bytes: float):
     import oracle
     t_start = time.time()
     samples = {}
-    # RMSNorm: 512 of the 8192 rows
-    xs = synth.bf16_bits(wl.x[0][:512])
+    # RMSNorm: CPU_RMS_ROWS of the 8192 rows
+    xs = synth.bf16_bits(wl.x[0][:CPU_RMS_ROWS])
     wln = synth.bf16_bits(wl.w_ln)
     t = time.perf_counter()
     oracle.rmsnorm(xs, wln, 1e-6)
-    samples["rmsnorm"] = (time.perf_counter() - t) * (RMS_ROWS / 512)
+    samples["rmsnorm"] = (time.perf_counter() - t) * (RMS_ROWS / CPU_RMS_ROWS)
     # matmul: rows of A against the full weight (the oracle's cost is linear in M)
     for nm, A, W in (("qkv", wl.a_qkv[0], wl.w_qkv[0]), ("oproj", wl.a_o[0], wl.w_o[0])):
-        m = 16
+        m = CPU_MM_ROWS
         a, w = synth.bf16_bits(A[:m]), synth.bf16_bits(W)
         t = time.perf_counter()
         oracle.matmul(a, w)
         samples["matmul_" + nm] = (time.perf_counter() - t) * (MM_M / m)
-    # attention: 8 requests (cost linear in their total length)
-    rows = list(range(8))
+    # attention: CPU_ATT_ROWS requests (cost linear in their total length)
+    rows = list(range(CPU_ATT_ROWS))
     kc, vc = synth.bf16_bits(wl.kv.k_cache), synth.bf16_bits(wl.kv.v_cache)
     bt = wl.kv.block_table.cpu().numpy()[rows]
     lens = np.array([wl.lens[r] for r in rows], dtype=np.int32)
@@ -234,12 +237,56 @@ def cpu_baseline(wl: Workload, step_bytes: float):
         "unit": "GB/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": ("fp64 C oracle (OpenMP) on 512 of 8192 RMSNorm rows, 16 of 4096 rows of "
-                   "each projection, 8 of 256 attention requests "
-                   f"({int(lens.sum())} KV tokens); each scaled linearly to the full step"),
+        "sample": (f"fp64 C oracle (OpenMP) on {CPU_RMS_ROWS} of 8192 RMSNorm rows, "
+                   f"{CPU_MM_ROWS} of 4096 rows of each projection, {CPU_ATT_ROWS} of 256 "
+                   f"attention requests ({int(lens.sum())} KV tokens); each scaled linearly "
+                   "to the full step"),
         "seconds_per_step_extrapolated": round(t_step, 2),
         "sample_wall_s": round(time.time() - t_start, 1),
     }
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_bi_b256_traffic.txt")
+ATTN_SRCS = [os.path.join(ROOT, "invariant_rmsnorm_bi_amd", "csrc", f)
+             for f in ("attention.hip", "device.h", "launch.h")]
+
+
+def attn_source_sha():
+    """sha256 over the sources the decode attention kernels are compiled from."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in ATTN_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode_attn_bi call from the committed FETCH_SIZE / WRITE_SIZE
+    summary (copy-calibrated), or None when that summary is missing or was taken on
+    a different attention source than the one built now."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != attn_source_sha():
+            return None
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe():
+    """A plain 1 GiB device-to-device copy, run 3 times: the known-size reference the
+    FETCH_SIZE / WRITE_SIZE counters are calibrated against."""
+    src = torch.empty(1 << 29, dtype=torch.bfloat16, device=DEV).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def fingerprint():
@@ -272,6 +319,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-twins", action="store_true", help="skip the tuned-twin comparison")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB copy (counter calibration for profiles/)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -322,8 +371,11 @@ def main():
     dom = kernels["decode_attn_bi"]
     roofline = {"bound": "hbm", "kernel": "decode_attn_bi (split + ordered merge)",
                 "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "algorithmic_bytes_per_launch": dom["bytes"], "avg_launch_us": dom["us"]}
+
+    if args.copy_probe:
+        copy_probe()
 
     twins = None
     if not args.no_twins:
