@@ -19,6 +19,8 @@
 // to fill 256 compute units, computes each range with the same tile kernel into
 // an fp32 workspace, and adds the ranges in ascending order: deterministic run
 // to run, but the K partition -- and so the bits -- changes with M.
+#include <cmath>
+
 #include "device.h"
 #include "launch.h"
 
@@ -430,40 +432,101 @@ hipError_t launch_tiles(const MatmulArgs &a, int splits, int64_t k_split, void *
 
 }  // namespace
 
+// Pipelined tile shapes and their measured throughput per unit of tile area (the
+// fraction of MFMA peak one full round of 256 workgroups reached on MI355X).
+struct TileCand {
+    int tbm, tbn;
+    double eff;
+};
+constexpr TileCand kTiles[] = {{256, 256, 0.56}, {256, 128, 0.42}, {128, 128, 0.39},
+                               {128, 64, 0.20},  {64, 64, 0.15},   {64, 32, 0.10}};
+constexpr int kNumTiles = 6;
+
+// (rounds of 256 workgroups) x (tile area) / (throughput per unit area)
+double tile_cost(int i, int64_t M, int64_t N)
+{
+    const TileCand &c = kTiles[i];
+    const int64_t tiles = ((M + c.tbm - 1) / c.tbm) * ((N + c.tbn - 1) / c.tbn);
+    return (double)((tiles + 255) / 256) * c.tbm * c.tbn / c.eff;
+}
+
+int best_tile(int64_t M, int64_t N, double *cost)
+{
+    int best = 0;
+    double bc = tile_cost(0, M, N);
+    for (int i = 1; i < kNumTiles; ++i) {
+        const double c = tile_cost(i, M, N);
+        if (c < bc) {
+            best = i;
+            bc = c;
+        }
+    }
+    *cost = bc;
+    return best;
+}
+
+hipError_t launch_tile_shape(int i, const MatmulArgs &a, hipStream_t s)
+{
+    switch (i) {
+    case 0: return launch_pipe<256, 256, 4, 4>(a, s);
+    case 1: return launch_pipe<256, 128, 2, 6>(a, s);
+    case 2: return launch_pipe<128, 128, 2, 8>(a, s);
+    case 3: return launch_pipe<128, 64, 2, 12>(a, s);
+    case 4: return launch_pipe<64, 64, 2, 8>(a, s);
+    default: return launch_pipe<64, 32, 1, 16>(a, s);
+    }
+}
+
 hipError_t launch_matmul_bi(const MatmulArgs &a, hipStream_t s)
 {
     // The tile shape is picked from the problem size; that changes which wave
-    // computes an element, never the element's arithmetic.  Each candidate is
-    // priced as (rounds of 256 workgroups) x (tile area) / (throughput per unit area
-    // measured for that tile on MI355X): big tiles are efficient once there are
-    // enough of them, small tiles keep all 256 compute units streaming weights when
-    // M is small.
+    // computes an element, never the element's arithmetic.  Big tiles are efficient
+    // once there are enough of them, small tiles keep all 256 compute units
+    // streaming weights when M is small.  When the best single shape would leave a
+    // last round of workgroups mostly empty, the columns are cut in two: the first
+    // N1 columns in full rounds of a big tile, the rest with the shape that suits
+    // them, as two launches on the same stream.
     if (a.K % PK == 0) {
-        struct Cand {
-            int tbm, tbn;
-            double eff;
-        };
-        static constexpr Cand cands[] = {{256, 256, 0.56}, {256, 128, 0.42}, {128, 128, 0.39},
-                                         {128, 64, 0.20},  {64, 64, 0.15},   {64, 32, 0.10}};
-        int best = 0;
-        double best_cost = 0;
-        for (int i = 0; i < 6; ++i) {
-            const Cand &c = cands[i];
+        double c1;
+        const int t1 = best_tile(a.M, a.N, &c1);
+        if (t1 <= 1) {
+            // a partly filled last round of big tiles runs faster than a full one
+            // (less contention); price it at sqrt(fill) of a round for this choice
+            const TileCand &c = kTiles[t1];
             const int64_t tiles = ((a.M + c.tbm - 1) / c.tbm) * ((a.N + c.tbn - 1) / c.tbn);
-            const double cost = (double)((tiles + 255) / 256) * c.tbm * c.tbn / c.eff;
-            if (i == 0 || cost < best_cost) {
-                best = i;
-                best_cost = cost;
+            const int64_t full = tiles / 256, rem = tiles % 256;
+            c1 = ((double)full + (rem ? std::sqrt(rem / 256.0) : 0.0)) * c.tbm * c.tbn / c.eff;
+        }
+        int split_t = -1, split_r = -1;
+        int64_t split_n = 0;
+        double best = c1;
+        for (int i = 0; i < 2; ++i) {  // the big shapes as the first part
+            const int64_t tbn = kTiles[i].tbn;
+            for (int64_t n1 = (a.N / tbn) * tbn; n1 >= tbn && n1 * 2 >= a.N; n1 -= tbn) {
+                if (n1 == a.N)
+                    continue;
+                double c2;
+                const int r = best_tile(a.M, a.N - n1, &c2);
+                const double c = tile_cost(i, a.M, n1) + c2;
+                if (c < best * 0.95) {  // a clear win only: two launches cost a little
+                    best = c;
+                    split_t = i;
+                    split_r = r;
+                    split_n = n1;
+                }
             }
         }
-        switch (best) {
-        case 0: return launch_pipe<256, 256, 4, 4>(a, s);
-        case 1: return launch_pipe<256, 128, 2, 6>(a, s);
-        case 2: return launch_pipe<128, 128, 2, 8>(a, s);
-        case 3: return launch_pipe<128, 64, 2, 12>(a, s);
-        case 4: return launch_pipe<64, 64, 2, 8>(a, s);
-        default: return launch_pipe<64, 32, 1, 16>(a, s);
-        }
+        if (split_t < 0)
+            return launch_tile_shape(t1, a, s);
+        MatmulArgs left = a, right = a;
+        left.N = split_n;
+        right.N = a.N - split_n;
+        right.W = a.W + split_n * a.ldw;
+        right.C = a.c_bf16 ? (void *)((uint16_t *)a.C + split_n) : (void *)((float *)a.C + split_n);
+        hipError_t e = launch_tile_shape(split_t, left, s);
+        if (e != hipSuccess)
+            return e;
+        return launch_tile_shape(split_r, right, s);
     }
     return launch_tiles(a, 1, a.K, a.C, a.ldc, a.c_bf16, 0, s);
 }
