@@ -187,12 +187,14 @@ int decode_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, con
 
 /*
  * decode_attn_tuned: same function, but the split size is chosen from the
- * batch shape so that the splits fill the chip, the "balanced scheduling" of
- * [P1] section 5.5 that the page names as not batch-invariant.
- * decode_attn_tuned_split_size() returns the size it will use; kv_lens_host
- * (optional, may be NULL) holds the rows' lengths on the host and sharpens the
- * choice.  The workspace is sized with decode_attn_workspace_size(..., that
- * split size).  Other arguments as decode_attn_bi.
+ * batch shape -- the per-batch scheduling of [P1] section 5.5 that the page
+ * names as not batch-invariant: a row's split boundaries, and so its bits, move
+ * with the batch.  The rule is the fastest split size measured on MI355X for
+ * these kernels: 1024 tokens for batches of at most 8 rows, 512 above (capped
+ * near max_kv_len).  decode_attn_tuned_split_size() returns the size it will use;
+ * kv_lens_host (optional, may be NULL) is accepted for API symmetry.  The
+ * workspace is sized with decode_attn_workspace_size(..., that split size).
+ * Other arguments as decode_attn_bi.
  */
 int decode_attn_tuned_split_size(int64_t rows, int num_kv_heads, int max_kv_len,
                                  const int32_t *kv_lens_host);

@@ -210,8 +210,17 @@ __device__ __forceinline__ void wait_loads_and_barrier()
 template <int TBM, int TBN, int WN, int P, bool OUT_BF16>
 __global__ __launch_bounds__(128 * WN, 1) void mm_pipe_kernel(
     const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restrict__ W, int64_t ldw,
-    void *__restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n)
+    void *__restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n,
+    int64_t k_split, int64_t c_split_stride)
 {
+    // split-K (blockIdx.y = range; the invariant path always has one range)
+    {
+        const int64_t kb0 = (int64_t)blockIdx.y * k_split;
+        A += kb0;
+        W += kb0;
+        K = (int)((K - kb0) < k_split ? (K - kb0) : k_split);
+        C = reinterpret_cast<char *>(C) + (int64_t)blockIdx.y * c_split_stride;
+    }
     constexpr int NW = 2 * WN;                   // waves
     constexpr int WTM = TBM / 2, WTN = TBN / WN; // wave tile
     constexpr int FM = WTM / 16, FN = WTN / 16;  // MFMA blocks per wave
@@ -366,8 +375,11 @@ __global__ __launch_bounds__(128 * WN, 1) void mm_pipe_kernel(
 }
 
 template <int TBM, int TBN, int WN, int P>
-hipError_t launch_pipe(const MatmulArgs &a, hipStream_t s)
+hipError_t launch_pipe(const MatmulArgs &a, hipStream_t s, int splits = 1, int64_t k_split = 0,
+                       int64_t c_split_stride = 0)
 {
+    if (splits == 1)
+        k_split = a.K;
     const int tiles_m = (int)((a.M + TBM - 1) / TBM), tiles_n = (int)((a.N + TBN - 1) / TBN);
     const size_t lds = (size_t)P * (TBM + TBN) * PK * sizeof(uint16_t);
     const void *fn = a.c_bf16 ? (const void *)mm_pipe_kernel<TBM, TBN, WN, P, true>
@@ -375,13 +387,15 @@ hipError_t launch_pipe(const MatmulArgs &a, hipStream_t s)
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess)
         return e;
-    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(128 * WN);
+    const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits), block(128 * WN);
     if (a.c_bf16)
         mm_pipe_kernel<TBM, TBN, WN, P, true><<<grid, block, lds, s>>>(
-            a.A, a.lda, a.W, a.ldw, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_m, tiles_n);
+            a.A, a.lda, a.W, a.ldw, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_m, tiles_n,
+            k_split, c_split_stride);
     else
         mm_pipe_kernel<TBM, TBN, WN, P, false><<<grid, block, lds, s>>>(
-            a.A, a.lda, a.W, a.ldw, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_m, tiles_n);
+            a.A, a.lda, a.W, a.ldw, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_m, tiles_n,
+            k_split, c_split_stride);
     return hipGetLastError();
 }
 
@@ -465,15 +479,16 @@ int best_tile(int64_t M, int64_t N, double *cost)
     return best;
 }
 
-hipError_t launch_tile_shape(int i, const MatmulArgs &a, hipStream_t s)
+hipError_t launch_tile_shape(int i, const MatmulArgs &a, hipStream_t s, int splits = 1,
+                             int64_t k_split = 0, int64_t c_split_stride = 0)
 {
     switch (i) {
-    case 0: return launch_pipe<256, 256, 4, 4>(a, s);
-    case 1: return launch_pipe<256, 128, 2, 6>(a, s);
-    case 2: return launch_pipe<128, 128, 2, 8>(a, s);
-    case 3: return launch_pipe<128, 64, 2, 12>(a, s);
-    case 4: return launch_pipe<64, 64, 2, 8>(a, s);
-    default: return launch_pipe<64, 32, 1, 16>(a, s);
+    case 0: return launch_pipe<256, 256, 4, 4>(a, s, splits, k_split, c_split_stride);
+    case 1: return launch_pipe<256, 128, 2, 6>(a, s, splits, k_split, c_split_stride);
+    case 2: return launch_pipe<128, 128, 2, 8>(a, s, splits, k_split, c_split_stride);
+    case 3: return launch_pipe<128, 64, 2, 12>(a, s, splits, k_split, c_split_stride);
+    case 4: return launch_pipe<64, 64, 2, 8>(a, s, splits, k_split, c_split_stride);
+    default: return launch_pipe<64, 32, 1, 16>(a, s, splits, k_split, c_split_stride);
     }
 }
 
@@ -531,24 +546,51 @@ hipError_t launch_matmul_bi(const MatmulArgs &a, hipStream_t s)
     return launch_tiles(a, 1, a.K, a.C, a.ldc, a.c_bf16, 0, s);
 }
 
-// Split count of the twin: enough K ranges that the tiles fill ~2 workgroups per
-// compute unit, each range at least 256 deep, at most 16 ranges.
+// Split count of the twin.  With K a multiple of 32 it takes the tile shape the
+// invariant path would pick and, when those tiles cannot fill half of the 256
+// compute units, cuts K into 2, 4, 8 or 16 equal ranges (each a multiple of 32, at
+// least 256 deep) until they fill them; otherwise the 128x128 tile kernel's count.
 int matmul_tuned_splits(int64_t M, int64_t N, int64_t K)
 {
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    int64_t tiles;
+    if (K % PK == 0) {
+        double c;
+        const TileCand &t = kTiles[best_tile(M, N, &c)];
+        tiles = ((M + t.tbm - 1) / t.tbm) * ((N + t.tbn - 1) / t.tbn);
+    } else {
+        tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    }
+    // only when the tiles leave at least half of the compute units idle: above
+    // that the fp32 partials' round trip costs more than the extra parallelism gains
+    if (tiles > 128)
+        return 1;
     int splits = 1;
-    while (splits < 16 && tiles * splits * 2 <= 512 && K / (splits * 2) >= 256)
+    while (splits < 16 && tiles * splits < 256 && K / (splits * 2) >= 256)
         splits *= 2;
     return splits;
 }
 
 hipError_t launch_matmul_splitk(const MatmulArgs &a, int splits, float *ws, hipStream_t s)
 {
-    // equal ranges, each a multiple of BK
+    if (splits <= 1)
+        return launch_matmul_bi(a, s);
+    // equal ranges, each a multiple of the kernel's k step
+    const int64_t step = (a.K % PK == 0) ? PK : BK;
     int64_t k_split = (a.K + splits - 1) / splits;
-    k_split = (k_split + BK - 1) / BK * BK;
+    k_split = (k_split + step - 1) / step * step;
     splits = (int)((a.K + k_split - 1) / k_split);
-    hipError_t e = launch_tiles(a, splits, k_split, ws, a.N, false, a.M * a.N * 4, s);
+    hipError_t e;
+    if (a.K % PK == 0) {
+        double c;
+        const int t = best_tile(a.M, a.N, &c);
+        MatmulArgs w = a;
+        w.C = ws;
+        w.ldc = a.N;
+        w.c_bf16 = false;
+        e = launch_tile_shape(t, w, s, splits, k_split, a.M * a.N * 4);
+    } else {
+        e = launch_tiles(a, splits, k_split, ws, a.N, false, a.M * a.N * 4, s);
+    }
     if (e != hipSuccess)
         return e;
     const int64_t nvec = a.M * (a.N / 4);

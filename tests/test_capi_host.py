@@ -79,7 +79,7 @@ def test_matmul_validation():
 def test_matmul_tuned_workspace_shape_dependence():
     # the twin splits K only when the output tiles cannot fill the chip
     assert rbi.matmul_tuned_workspace_size(4096, 9216, 4096) == 0
-    assert rbi.matmul_tuned_workspace_size(1, 9216, 4096) > 0
+    assert rbi.matmul_tuned_workspace_size(1, 4096, 8192) > 0
     assert rbi.matmul_tuned_workspace_size(0, 9216, 4096) == 0
 
 
@@ -122,12 +122,16 @@ def test_decode_attn_workspace_depends_only_on_bounds():
 
 
 def test_tuned_split_size_follows_the_batch():
-    # balanced scheduling: long single request -> small splits; big batch -> large
+    # the twin's split size moves with the batch (the fixed-size kernel would use
+    # 256 for every batch)
     one = rbi.decode_attn_tuned_split_size(1, 4, 32768, [32768])
     many = rbi.decode_attn_tuned_split_size(256, 4, 32768, [32768] * 256)
-    assert one <= 256 and many == 1024
-    assert one % 16 == 0 and many % 16 == 0
-    # the fixed-size kernel would use 256 in both cases
+    assert one == 1024 and many == 512
+    assert rbi.decode_attn_tuned_split_size(8, 4, 32768, None) == 1024
+    assert rbi.decode_attn_tuned_split_size(9, 4, 32768, None) == 512
+    # capped near short maximum lengths, always a multiple of the page
+    short = rbi.decode_attn_tuned_split_size(1, 4, 100, None)
+    assert short % 16 == 0 and 16 <= short <= 128
 
 
 def test_kv_append_and_glue_validation():
