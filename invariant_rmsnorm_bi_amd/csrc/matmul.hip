@@ -169,8 +169,8 @@ __global__ __launch_bounds__(256, 2) void mm_tile_kernel(
     }
 }
 
-// Pipelined large-tile kernel for K a multiple of 32: a TBM x TBN output tile per
-// workgroup of 2*WN waves in a 2 x WN grid, each wave owning (TBM/2) batch rows x
+// Pipelined tile kernel for K a multiple of 32: a TBM x TBN output tile per
+// workgroup of WM*WN waves in a WM x WN grid, each wave owning (TBM/WM) batch rows x
 // (TBN/WN) features.  K advances one MFMA step (32 k) per stage; P stages of
 // operand tiles are in flight at once, copied from global memory straight into LDS
 // (global_load_lds_dwordx4: no register staging), so a load has P-1 stages of MFMA
@@ -207,8 +207,8 @@ __device__ __forceinline__ void wait_loads_and_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <int TBM, int TBN, int WN, int P, bool OUT_BF16>
-__global__ __launch_bounds__(128 * WN, 1) void mm_pipe_kernel(
+template <int TBM, int TBN, int WM, int WN, int P, bool OUT_BF16>
+__global__ __launch_bounds__(64 * WM * WN, 1) void mm_pipe_kernel(
     const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restrict__ W, int64_t ldw,
     void *__restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n,
     int64_t k_split, int64_t c_split_stride)
@@ -221,14 +221,14 @@ __global__ __launch_bounds__(128 * WN, 1) void mm_pipe_kernel(
         K = (int)((K - kb0) < k_split ? (K - kb0) : k_split);
         C = reinterpret_cast<char *>(C) + (int64_t)blockIdx.y * c_split_stride;
     }
-    constexpr int NW = 2 * WN;                   // waves
-    constexpr int WTM = TBM / 2, WTN = TBN / WN; // wave tile
+    constexpr int NW = WM * WN;                   // waves
+    constexpr int WTM = TBM / WM, WTN = TBN / WN; // wave tile
     constexpr int FM = WTM / 16, FN = WTN / 16;  // MFMA blocks per wave
     constexpr int ROWS = TBM + TBN;
     constexpr int STAGE = ROWS * PK;             // bf16 elements per stage
     constexpr int LPW = ROWS / (16 * NW);        // 16-row load instructions per wave per stage
-    static_assert(ROWS % (16 * NW) == 0 && TBM % (16 * NW) == 0 && WTN % 16 == 0 &&
-                      WTM % 16 == 0, "tile shape");
+    static_assert(ROWS % (16 * NW) == 0 && TBM % 16 == 0 && WTN % 16 == 0 && WTM % 16 == 0,
+                  "tile shape");
     static_assert(P >= 3, "pipeline depth");
     extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
 
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(128 * WN, 1) void mm_pipe_kernel(
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % WM, wn = wave / WM;
     const int lr = lane & 15, lq = lane >> 4;
 
     // source of this lane's 16 bytes in load instruction i of a stage (k = 0); rows
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(128 * WN, 1) void mm_pipe_kernel(
     }
 }
 
-template <int TBM, int TBN, int WN, int P>
+template <int TBM, int TBN, int WM, int WN, int P>
 hipError_t launch_pipe(const MatmulArgs &a, hipStream_t s, int splits = 1, int64_t k_split = 0,
                        int64_t c_split_stride = 0)
 {
@@ -382,18 +382,18 @@ hipError_t launch_pipe(const MatmulArgs &a, hipStream_t s, int splits = 1, int64
         k_split = a.K;
     const int tiles_m = (int)((a.M + TBM - 1) / TBM), tiles_n = (int)((a.N + TBN - 1) / TBN);
     const size_t lds = (size_t)P * (TBM + TBN) * PK * sizeof(uint16_t);
-    const void *fn = a.c_bf16 ? (const void *)mm_pipe_kernel<TBM, TBN, WN, P, true>
-                              : (const void *)mm_pipe_kernel<TBM, TBN, WN, P, false>;
+    const void *fn = a.c_bf16 ? (const void *)mm_pipe_kernel<TBM, TBN, WM, WN, P, true>
+                              : (const void *)mm_pipe_kernel<TBM, TBN, WM, WN, P, false>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess)
         return e;
-    const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits), block(128 * WN);
+    const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits), block(64 * WM * WN);
     if (a.c_bf16)
-        mm_pipe_kernel<TBM, TBN, WN, P, true><<<grid, block, lds, s>>>(
+        mm_pipe_kernel<TBM, TBN, WM, WN, P, true><<<grid, block, lds, s>>>(
             a.A, a.lda, a.W, a.ldw, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_m, tiles_n,
             k_split, c_split_stride);
     else
-        mm_pipe_kernel<TBM, TBN, WN, P, false><<<grid, block, lds, s>>>(
+        mm_pipe_kernel<TBM, TBN, WM, WN, P, false><<<grid, block, lds, s>>>(
             a.A, a.lda, a.W, a.ldw, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_m, tiles_n,
             k_split, c_split_stride);
     return hipGetLastError();
@@ -453,8 +453,10 @@ struct TileCand {
     double eff;
 };
 constexpr TileCand kTiles[] = {{256, 256, 0.56}, {256, 128, 0.42}, {128, 128, 0.39},
-                               {128, 64, 0.20},  {64, 64, 0.15},   {64, 32, 0.10}};
-constexpr int kNumTiles = 6;
+                               {128, 64, 0.20},  {64, 64, 0.15},   {64, 32, 0.10},
+                               {16, 16, 0.0},    {32, 16, 0.0}};
+constexpr int kNumTiles = 6;  // priced by the cost model; the last two are one-wave
+                              // weight-streaming tiles for small M (rule below)
 
 // (rounds of 256 workgroups) x (tile area) / (throughput per unit area)
 double tile_cost(int i, int64_t M, int64_t N)
@@ -466,6 +468,20 @@ double tile_cost(int i, int64_t M, int64_t N)
 
 int best_tile(int64_t M, int64_t N, double *cost)
 {
+    // Small M is a weight stream: one-wave 16-row tiles give every compute unit
+    // several independent streams.  16 x 16 while there are at most 1024 of them,
+    // else 32 x 16 up to M = 32 (measured on the attention projections).
+    if (M <= 64) {
+        const int64_t t16 = ((M + 15) / 16) * ((N + 15) / 16);
+        if (t16 <= 1024) {
+            *cost = 0;
+            return 6;
+        }
+        if (M <= 32) {
+            *cost = 0;
+            return 7;
+        }
+    }
     int best = 0;
     double bc = tile_cost(0, M, N);
     for (int i = 1; i < kNumTiles; ++i) {
@@ -483,12 +499,14 @@ hipError_t launch_tile_shape(int i, const MatmulArgs &a, hipStream_t s, int spli
                              int64_t k_split = 0, int64_t c_split_stride = 0)
 {
     switch (i) {
-    case 0: return launch_pipe<256, 256, 4, 4>(a, s, splits, k_split, c_split_stride);
-    case 1: return launch_pipe<256, 128, 2, 6>(a, s, splits, k_split, c_split_stride);
-    case 2: return launch_pipe<128, 128, 2, 8>(a, s, splits, k_split, c_split_stride);
-    case 3: return launch_pipe<128, 64, 2, 12>(a, s, splits, k_split, c_split_stride);
-    case 4: return launch_pipe<64, 64, 2, 8>(a, s, splits, k_split, c_split_stride);
-    default: return launch_pipe<64, 32, 1, 16>(a, s, splits, k_split, c_split_stride);
+    case 0: return launch_pipe<256, 256, 2, 4, 4>(a, s, splits, k_split, c_split_stride);
+    case 1: return launch_pipe<256, 128, 2, 2, 6>(a, s, splits, k_split, c_split_stride);
+    case 2: return launch_pipe<128, 128, 2, 2, 8>(a, s, splits, k_split, c_split_stride);
+    case 3: return launch_pipe<128, 64, 2, 2, 12>(a, s, splits, k_split, c_split_stride);
+    case 4: return launch_pipe<64, 64, 2, 2, 8>(a, s, splits, k_split, c_split_stride);
+    case 5: return launch_pipe<64, 32, 2, 1, 16>(a, s, splits, k_split, c_split_stride);
+    case 6: return launch_pipe<16, 16, 1, 1, 16>(a, s, splits, k_split, c_split_stride);
+    default: return launch_pipe<32, 16, 1, 1, 16>(a, s, splits, k_split, c_split_stride);
     }
 }
 
@@ -522,6 +540,8 @@ hipError_t launch_matmul_bi(const MatmulArgs &a, hipStream_t s)
                     continue;
                 double c2;
                 const int r = best_tile(a.M, a.N - n1, &c2);
+                if (r >= kNumTiles)
+                    continue;  // small-M tiles are not priced; keep one launch
                 const double c = tile_cost(i, a.M, n1) + c2;
                 if (c < best * 0.95) {  // a clear win only: two launches cost a little
                     best = c;
@@ -547,25 +567,31 @@ hipError_t launch_matmul_bi(const MatmulArgs &a, hipStream_t s)
 }
 
 // Split count of the twin.  With K a multiple of 32 it takes the tile shape the
-// invariant path would pick and, when those tiles cannot fill half of the 256
-// compute units, cuts K into 2, 4, 8 or 16 equal ranges (each a multiple of 32, at
-// least 256 deep) until they fill them; otherwise the 128x128 tile kernel's count.
+// invariant path would pick and cuts K into 2, 4, 8 or 16 equal ranges (each a
+// multiple of 32, at least 256 deep) until the workgroups fill the chip: ~1024 of
+// the one-wave small-M tiles, 256 of the bigger ones, whose partials only pay off
+// when their tiles leave half of the compute units idle.  Otherwise the 128x128
+// tile kernel's count.
 int matmul_tuned_splits(int64_t M, int64_t N, int64_t K)
 {
-    int64_t tiles;
+    int64_t tiles, target = 256;
     if (K % PK == 0) {
         double c;
-        const TileCand &t = kTiles[best_tile(M, N, &c)];
+        const int ti = best_tile(M, N, &c);
+        const TileCand &t = kTiles[ti];
         tiles = ((M + t.tbm - 1) / t.tbm) * ((N + t.tbn - 1) / t.tbn);
+        if (ti >= kNumTiles) {
+            target = 1024;  // one-wave weight-streaming tiles: ~4 per compute unit
+        } else if (tiles > 128) {
+            // multi-wave tiles filling at least half of the compute units: the fp32
+            // partials' round trip costs more than the extra parallelism gains
+            return 1;
+        }
     } else {
         tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     }
-    // only when the tiles leave at least half of the compute units idle: above
-    // that the fp32 partials' round trip costs more than the extra parallelism gains
-    if (tiles > 128)
-        return 1;
     int splits = 1;
-    while (splits < 16 && tiles * splits < 256 && K / (splits * 2) >= 256)
+    while (splits < 16 && tiles * splits < target && K / (splits * 2) >= 256)
         splits *= 2;
     return splits;
 }
