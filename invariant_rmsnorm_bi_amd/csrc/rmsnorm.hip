@@ -122,19 +122,21 @@ __device__ __forceinline__ float inv_rms(float sumsq, int64_t H, float eps)
     return 1.0f / sqrtf(ms + eps);
 }
 
-// One wavefront per row, four rows per 256-thread workgroup.  Rows of up to
-// 64*CPL chunks stay in registers between the two passes; longer rows are read
-// twice.  Both paths execute the same arithmetic in the same order.
-template <bool BF16, int CPL>
-__global__ __launch_bounds__(256) void rmsnorm_wave_kernel(const char *x, int64_t xs,
-                                                           const char *__restrict__ w, char *y,
-                                                           int64_t ys, int64_t rows, int64_t H,
-                                                           float eps)
+// One wavefront per row, RPW rows per workgroup (one row per workgroup for small
+// batches, so that even 256 rows reach 256 compute units).  Rows of up to 64*CPL
+// chunks stay in registers between the two passes; longer rows are read twice.
+// Both paths execute the same arithmetic in the same order.
+template <bool BF16, int CPL, int RPW>
+__global__ __launch_bounds__(64 * RPW) void rmsnorm_wave_kernel(const char *x, int64_t xs,
+                                                                const char *__restrict__ w,
+                                                                char *y, int64_t ys,
+                                                                int64_t rows, int64_t H,
+                                                                float eps)
 {
     constexpr int VEC = Elt<BF16>::VEC;
     constexpr int SZ = Elt<BF16>::SIZE;
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * RPW + (threadIdx.x >> 6);
     if (row >= rows)
         return;
     const char *xr = x + row * xs * SZ;
@@ -232,13 +234,24 @@ hipError_t launch_rmsnorm_wave(const void *x, int64_t xs, const void *w, void *y
                                int64_t rows, int64_t hidden, float eps, bool bf16,
                                hipStream_t s)
 {
-    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-    if (bf16)
-        rmsnorm_wave_kernel<true, 8><<<grid, block, 0, s>>>(
-            (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
-    else
-        rmsnorm_wave_kernel<false, 8><<<grid, block, 0, s>>>(
-            (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
+    // the workgroup size changes with the batch, never a row's arithmetic
+    if (rows >= 4096) {
+        const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+        if (bf16)
+            rmsnorm_wave_kernel<true, 8, 4><<<grid, block, 0, s>>>(
+                (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
+        else
+            rmsnorm_wave_kernel<false, 8, 4><<<grid, block, 0, s>>>(
+                (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
+    } else {
+        const dim3 grid((unsigned)rows), block(64);
+        if (bf16)
+            rmsnorm_wave_kernel<true, 8, 1><<<grid, block, 0, s>>>(
+                (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
+        else
+            rmsnorm_wave_kernel<false, 8, 1><<<grid, block, 0, s>>>(
+                (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
+    }
     return hipGetLastError();
 }
 
