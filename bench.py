@@ -198,6 +198,57 @@ def twin_points(wl: Workload):
     return pts
 
 
+def layer_points():
+    """End-to-end decode step of the dense layer (hidden 4096, 64/4 heads of 128,
+    SwiGLU 12288, lm_head 151936, greedy argmax) built from the bi kernels versus
+    the same layer built from the tuned twins, at batch sizes 1, 16, 64 and 128;
+    each request has its own pages and a KV length ~ U{1..4096} (the cache holds
+    seeded random K/V).  Wall clock per step (host scheduling included, the same
+    for both), median of 10 after 3 warmup steps."""
+    from invariant_rmsnorm_bi_amd.layer import DecodeLayer, LayerConfig
+    cfg = LayerConfig()
+    w = synth.dense_layer_weights(cfg.hidden, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                                  cfg.intermediate, cfg.vocab, device=DEV)
+    rng = np.random.default_rng(synth.SEED_BATCH)
+    Bmax, lmax = 128, 4096
+    pages_per = lmax // cfg.page_size
+    layers = {}
+    for tuned in (False, True):
+        layers[tuned] = DecodeLayer(cfg, w, num_pages=Bmax * pages_per, device=DEV, tuned=tuned)
+    kc = synth.normal(tuple(layers[False].k_cache.shape), seed=60, device=DEV)
+    vc = synth.normal(tuple(layers[False].v_cache.shape), seed=61, device=DEV)
+    for tuned in (False, True):
+        layers[tuned].k_cache.copy_(kc)
+        layers[tuned].v_cache.copy_(vc)
+    del kc, vc
+    table = np.zeros((Bmax, cfg.max_kv_len // cfg.page_size), dtype=np.int32)
+    for r in range(Bmax):
+        table[r, :pages_per] = np.arange(r * pages_per, (r + 1) * pages_per)
+    pos = rng.integers(0, lmax, size=Bmax)
+    toks = rng.integers(0, cfg.vocab, size=Bmax)
+    pts = []
+    for B in (1, 16, 64, 128):
+        t = {}
+        for tuned in (False, True):
+            ly = layers[tuned]
+            for _ in range(3):
+                ly.step(toks[:B], table[:B], pos[:B])
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(10):
+                t0 = time.perf_counter()
+                ly.step(toks[:B], table[:B], pos[:B])
+                torch.cuda.synchronize()
+                ts.append(time.perf_counter() - t0)
+            t[tuned] = float(np.median(ts)) * 1e6
+        pts.append({"point": f"layer step B={B}", "bi_us": round(t[False], 1),
+                    "tuned_us": round(t[True], 1),
+                    "slowdown_pct": round((t[False] / t[True] - 1) * 100, 2)})
+    del layers, w
+    torch.cuda.empty_cache()
+    return pts
+
+
 # --------------------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample of the same workload)
 # --------------------------------------------------------------------------------------
@@ -319,6 +370,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-twins", action="store_true", help="skip the tuned-twin comparison")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the end-to-end decode-layer comparison")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB copy (counter calibration for profiles/)")
     args = ap.parse_args()
@@ -388,6 +441,11 @@ def main():
         mean = float(np.mean([p["slowdown_pct"] for p in pts]))
         twins = {"points": pts, "mean_slowdown_pct": round(mean, 2),
                  "unit": "time increase of bi over tuned, percent"}
+        if not args.no_layer:
+            log("timing the decode layer, bi against tuned")
+            lp = layer_points()
+            twins["layer"] = {"points": lp, "mean_slowdown_pct": round(
+                float(np.mean([p["slowdown_pct"] for p in lp])), 2)}
 
     cpu = None
     if not args.no_cpu:

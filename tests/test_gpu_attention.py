@@ -87,6 +87,29 @@ def test_c4_heads_parity(lens):
         assert ok, (fn.__name__, ratio, row)
 
 
+@pytest.mark.parametrize("d,hq,hkv,split", [(64, 8, 1, 1024), (128, 16, 2, 512), (64, 32, 4, 64),
+                                             (128, 4, 4, 16), (128, 64, 8, 1024)])
+def test_shapes_and_split_sizes(d, hq, hkv, split):
+    # head_dim 64 and 128, groups of 1, 2, 8 and 16 query heads, split sizes from one
+    # page to 1024 tokens (up to 16 page pairs per wave); lengths straddle split and
+    # page boundaries and reach max_kv_len exactly.  Parity per row, and every row
+    # alone equals its row in the batch.
+    lens = [1, split - 1, split, split + 1, 3 * split + 7, 2500]
+    kv = _to(synth.paged_kv(lens, hkv, d, 16, seed=7))
+    q = synth.normal((len(lens), hq, d), seed=8).to(DEV)
+    scale = 1 / math.sqrt(d)
+    L = max(lens)
+    out = _run(rbi.decode_attn_bi, q, kv, L, split_size=split, scale=scale)
+    ok, ratio, row = _tol_ok(out, _oracle(q, kv, scale))
+    assert ok, (ratio, row)
+    for r in (0, 2, 5):
+        sub = synth.PagedKV(kv.k_cache, kv.v_cache, kv.block_table[r:r + 1].contiguous(),
+                            kv.kv_lens[r:r + 1].contiguous(), 16, hkv, d)
+        alone = _run(rbi.decode_attn_bi, q[r:r + 1].contiguous(), sub, L, split_size=split,
+                     scale=scale)
+        assert torch.equal(alone[0], out[r]), r
+
+
 def test_single_token_is_exact():
     # L = 1: the softmax weight is exactly 1, so the output is v_0 bit for bit
     kv = _to(synth.paged_kv([1, 1, 1], 4, 128, 16))
