@@ -253,7 +253,7 @@ def layer_points():
 # CPU oracle baseline (bounded sample of the same workload)
 # --------------------------------------------------------------------------------------
 
-CPU_RMS_ROWS, CPU_MM_ROWS, CPU_ATT_ROWS = 2048, 96, 48
+CPU_RMS_ROWS, CPU_MM_ROWS, CPU_ATT_ROWS = 8192, 384, 192
 
 
 def cpu_baseline(wl: Workload, step_bytes: float):
