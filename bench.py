@@ -204,8 +204,9 @@ def layer_points():
     the same layer built from the tuned twins, at batch sizes 1, 16, 64 and 128;
     each request has its own pages and a KV length ~ U{1..4096} (the cache holds
     seeded random K/V).  Wall clock per step (host scheduling included, the same
-    for both), median of 10 after 3 warmup steps."""
-    from invariant_rmsnorm_bi_amd.layer import DecodeLayer, LayerConfig
+    for both), median of 10 after 3 warmup steps; also the bi step replayed as a
+    captured HIP graph (same kernels, no per-launch host cost)."""
+    from invariant_rmsnorm_bi_amd.layer import DecodeLayer, GraphedStep, LayerConfig
     cfg = LayerConfig()
     w = synth.dense_layer_weights(cfg.hidden, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
                                   cfg.intermediate, cfg.vocab, device=DEV)
@@ -241,9 +242,23 @@ def layer_points():
                 torch.cuda.synchronize()
                 ts.append(time.perf_counter() - t0)
             t[tuned] = float(np.median(ts)) * 1e6
+        # the bi step captured as a HIP graph: same kernels, no per-launch host cost
+        g = GraphedStep(layers[False], table[:B], pos[:B], toks[:B])
+        for _ in range(3):
+            g.step(toks[:B], pos[:B])
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(10):
+            t0 = time.perf_counter()
+            g.step(toks[:B], pos[:B])
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        t_graph = float(np.median(ts)) * 1e6
+        del g
         pts.append({"point": f"layer step B={B}", "bi_us": round(t[False], 1),
                     "tuned_us": round(t[True], 1),
-                    "slowdown_pct": round((t[False] / t[True] - 1) * 100, 2)})
+                    "slowdown_pct": round((t[False] / t[True] - 1) * 100, 2),
+                    "bi_graph_us": round(t_graph, 1)})
     del layers, w
     torch.cuda.empty_cache()
     return pts
@@ -253,7 +268,7 @@ def layer_points():
 # CPU oracle baseline (bounded sample of the same workload)
 # --------------------------------------------------------------------------------------
 
-CPU_RMS_ROWS, CPU_MM_ROWS, CPU_ATT_ROWS = 8192, 384, 192
+CPU_RMS_ROWS, CPU_MM_ROWS, CPU_ATT_ROWS = 8192, 768, 256
 
 
 def cpu_baseline(wl: Workload, step_bytes: float):

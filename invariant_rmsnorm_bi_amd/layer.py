@@ -69,22 +69,32 @@ class DecodeLayer:
     def _norm(self, x, w):
         return (rmsnorm_tuned if self.tuned else rmsnorm_bi)(x, w, self.cfg.eps)
 
-    def step(self, tokens, block_table: np.ndarray, positions) -> tuple[torch.Tensor, torch.Tensor]:
-        """Run rows (tokens[i] at positions[i] of the request whose block table is
-        block_table[i]).  Returns (fp32 logits [B, vocab], argmax tokens [B] int32)."""
+    def schedule(self, block_table: np.ndarray, positions):
+        """Host bookkeeping of a step: the cache slot each row's new token goes to
+        and each row's KV length (position + 1)."""
         c = self.cfg
-        dev = self.device
         positions = np.asarray(positions, dtype=np.int64)
         bt = np.ascontiguousarray(block_table, dtype=np.int32)
         B = positions.shape[0]
         slots = bt[np.arange(B), positions // c.page_size].astype(np.int64) * c.page_size \
             + positions % c.page_size
-        lens_h = (positions + 1).astype(np.int32)
-        tok = torch.as_tensor(np.asarray(tokens, dtype=np.int32)).to(dev, non_blocking=False)
-        bt_d = torch.from_numpy(bt).to(dev)
-        slots_d = torch.from_numpy(slots.astype(np.int32)).to(dev)
-        lens_d = torch.from_numpy(lens_h).to(dev)
+        return bt, slots.astype(np.int32), (positions + 1).astype(np.int32)
 
+    def step(self, tokens, block_table: np.ndarray, positions) -> tuple[torch.Tensor, torch.Tensor]:
+        """Run rows (tokens[i] at positions[i] of the request whose block table is
+        block_table[i]).  Returns (fp32 logits [B, vocab], argmax tokens [B] int32)."""
+        dev = self.device
+        bt, slots, lens_h = self.schedule(block_table, positions)
+        tok = torch.as_tensor(np.asarray(tokens, dtype=np.int32)).to(dev, non_blocking=False)
+        return self.forward(tok, torch.from_numpy(bt).to(dev), torch.from_numpy(slots).to(dev),
+                            torch.from_numpy(lens_h).to(dev), lens_h)
+
+    def forward(self, tok, bt_d, slots_d, lens_d, lens_h):
+        """The device part of a step on device inputs (token ids, block tables, cache
+        slots, KV lengths); lens_h, the lengths on the host, only steers the twin's
+        split size."""
+        c = self.cfg
+        B = tok.shape[0]
         x = embed(self.w["embed"], tok)
         a = self._norm(x, self.w["ln1"])
         qkv = self._mm(a, self.w["wqkv"])
@@ -107,3 +117,46 @@ class DecodeLayer:
         o2 = residual_add(h, dn)
         logits = self._mm(o2, self.w["lm_head"], out_dtype=torch.float32)
         return logits, argmax_rows(logits)
+
+
+class GraphedStep:
+    """A decode step of one batch shape captured once as a HIP graph (through
+    torch's graph capture of the library's stream launches) and replayed with new
+    tokens and positions.  The block tables are fixed at capture; tokens, cache
+    slots and KV lengths are copied into the captured input buffers before each
+    replay.  Every kernel is the same one the eager step launches, so a replay
+    gives the eager step's bits; the graph only removes per-launch host overhead.
+    For the twins the split size is fixed by the batch size at capture."""
+
+    def __init__(self, layer: DecodeLayer, block_table: np.ndarray, positions, tokens):
+        dev = layer.device
+        self.layer = layer
+        bt, slots, lens_h = layer.schedule(block_table, positions)
+        self.bt_h = bt
+        self.bt = torch.from_numpy(bt).to(dev)
+        self.tok = torch.as_tensor(np.asarray(tokens, dtype=np.int32)).to(dev)
+        self.slots = torch.from_numpy(slots).to(dev)
+        self.lens = torch.from_numpy(lens_h).to(dev)
+        self.lens_h = lens_h
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm up outside the capture
+            layer.forward(self.tok, self.bt, self.slots, self.lens, lens_h)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.logits, self.tokens = layer.forward(self.tok, self.bt, self.slots, self.lens,
+                                                     lens_h)
+        torch.cuda.synchronize()
+
+    def step(self, tokens, positions) -> tuple[torch.Tensor, torch.Tensor]:
+        """Replay with new tokens and positions (same rows, same block tables).
+        Returns the captured output buffers (overwritten by the next replay)."""
+        _, slots, lens_h = self.layer.schedule(self.bt_h, positions)
+        self.tok.copy_(torch.as_tensor(np.asarray(tokens, dtype=np.int32)))
+        self.slots.copy_(torch.from_numpy(slots))
+        self.lens.copy_(torch.from_numpy(lens_h))
+        self.graph.replay()
+        return self.logits, self.tokens
+

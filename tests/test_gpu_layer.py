@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from invariant_rmsnorm_bi_amd.layer import DecodeLayer, LayerConfig
+from invariant_rmsnorm_bi_amd.layer import DecodeLayer, GraphedStep, LayerConfig
 from oracle.layer import DenseLayerOracle, LayerDims
 
 pytestmark = pytest.mark.gpu
@@ -182,3 +182,29 @@ def test_layer_matches_oracle_short_prompt(weights):
         g_lg, g_tok = layer.step([gt], table[None], [p])
         o_lg, o_tok = orc.step([gt], table[None], [p])
     assert len(seq) >= 1
+
+
+def test_graph_replay_equals_eager_steps(weights):
+    # The step captured as a HIP graph and replayed 12 times (tokens fed back, KV
+    # growing across the 256-token split boundary for one row) gives the eager
+    # step's logits and tokens bit for bit; eager work runs between the replays.
+    B, steps = 5, 12
+    rng = np.random.default_rng(5)
+    pages = 40
+    table = np.stack([_table(list(range(r * pages, (r + 1) * pages))) for r in range(B)])
+    pos = np.array([0, 17, 250, 300, 511])
+    tok = rng.integers(0, CFG.vocab, B)
+    eager = DecodeLayer(CFG, weights, num_pages=B * pages)
+    graphed_layer = DecodeLayer(CFG, weights, num_pages=B * pages)
+    g = GraphedStep(graphed_layer, table, pos, tok)
+    # the capture's warmup ran the first step once on the graphed layer's cache;
+    # the eager layer runs it now, so both caches hold the same first-step K/V
+    eager.step(tok, table, pos)
+    for i in range(steps):
+        lg_e, tk_e = eager.step(tok, table, pos + i)
+        lg_g, tk_g = g.step(tok, pos + i)
+        torch.cuda.synchronize()
+        assert torch.equal(lg_e, lg_g), i
+        assert torch.equal(tk_e, tk_g), i
+        tok = tk_e.cpu().numpy()
+
