@@ -1,6 +1,7 @@
 """Benchmark of the batch-invariant forward reductions on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-twins]
+                    [--no-layer] [--no-prefill] [--copy-probe]
 
 A *step* is one pass of the whole hot path over one batch of synthetic
 Qwen3-235B-A22B-shaped input, every kernel batch-invariant:
@@ -17,7 +18,8 @@ serve them warm.  ``value`` = algorithmic HBM bytes of the step / step time.
 Printed: ONE JSON line with the metric, a per-kernel breakdown (HBM GB/s or MFMA
 TFLOP/s against the chip's peak), the ``roofline`` object of the dominant kernel
 (decode attention), the shape-tuned twins' times and the determinism slowdown
-(t_bi / t_tuned - 1), and the CPU oracle timed on a bounded sample of the same
+(t_bi / t_tuned - 1), prefill attention against the same tokens as decode rows,
+and the CPU oracle timed on a bounded sample of the same
 workload (``cpu_baseline``).
 """
 from __future__ import annotations
@@ -264,6 +266,49 @@ def layer_points():
     return pts
 
 
+PREFILL_POINTS = ((0, 4096), (2048, 2048), (0, 1024), (8000, 64))
+
+
+def prefill_points():
+    """prefill_attn_bi on one request's prompt chunk (64 query / 4 kv heads of 128,
+    page 16, split 256; the chunk's K/V already in the cache, pages placed by a
+    seeded permutation) against the same tokens run as decode_attn_bi rows
+    (kv_len = position + 1): device time (median of 20), the algorithmic MFMA
+    work 4 * Hq * D * sum(L_t) as TFLOP/s and its fraction of the bf16 peak, and
+    whether every output bit agrees."""
+    pts = []
+    for start, T in PREFILL_POINTS:
+        total = start + T
+        npages = -(-total // PAGE)
+        pages = synth.page_ids(npages + 8, seed=70)[:npages].to(torch.int32).to(DEV)
+        kc = synth.normal((npages + 8, HKV, PAGE, D), seed=71, device=DEV)
+        vc = synth.normal((npages + 8, HKV, D, PAGE), seed=72, device=DEV)
+        q = synth.normal((T, HQ, D), seed=73, device=DEV)
+        need = rbi.prefill_attn_workspace_size(T, HQ, HKV, D, start, SPLIT)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+        out_p = torch.empty_like(q)
+        t_p = time_fn(lambda: rbi.prefill_attn_bi(q, kc, vc, pages, start, SPLIT, out=out_p,
+                                                  workspace=ws))
+        bt = pages[None].repeat(T, 1).contiguous()
+        lens = torch.arange(start + 1, total + 1, dtype=torch.int32, device=DEV)
+        ws_d = torch.empty(rbi.decode_attn_workspace_size(T, HQ, D, total, SPLIT),
+                           dtype=torch.uint8, device=DEV)
+        out_d = torch.empty_like(q)
+        t_d = time_fn(lambda: rbi.decode_attn_bi(q, kc, vc, bt, lens, total, SPLIT, out=out_d,
+                                                 workspace=ws_d))
+        flops = 4 * HQ * D * (T * start + T * (T + 1) // 2)
+        tf = flops / (t_p * 1e-3) / 1e12
+        pts.append({"point": f"prefill start={start} tokens={T}",
+                    "schedule": "fused" if need == 0 else "split",
+                    "prefill_us": round(t_p * 1e3, 1), "decode_rows_us": round(t_d * 1e3, 1),
+                    "speedup": round(t_d / t_p, 2), "flops": flops, "TFLOP/s": round(tf, 1),
+                    "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFS, 4),
+                    "bitwise_equal_to_decode_rows": bool(torch.equal(out_p, out_d))})
+        del kc, vc, q, ws, ws_d, out_p, out_d, bt
+        torch.cuda.empty_cache()
+    return pts
+
+
 # --------------------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample of the same workload)
 # --------------------------------------------------------------------------------------
@@ -387,6 +432,8 @@ def main():
     ap.add_argument("--no-twins", action="store_true", help="skip the tuned-twin comparison")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the end-to-end decode-layer comparison")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill-attention comparison")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB copy (counter calibration for profiles/)")
     args = ap.parse_args()
@@ -462,6 +509,12 @@ def main():
             twins["layer"] = {"points": lp, "mean_slowdown_pct": round(
                 float(np.mean([p["slowdown_pct"] for p in lp])), 2)}
 
+    prefill = None
+    if not args.no_prefill:
+        log("timing prefill attention against decode rows")
+        prefill = {"points": prefill_points(),
+                   "unit": "device us; TFLOP/s of the algorithmic 4*Hq*D*sum(L) MFMA work"}
+
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample")
@@ -478,6 +531,7 @@ def main():
                                 "(64q/4kv heads, d128, page 16, split 256, L~U{1..32768})"),
                    "step_bytes": step_bytes, "buffer_sets": SETS},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "twins": twins,
+        "prefill": prefill,
         "fingerprint": fingerprint(),
     }
     print(json.dumps(rec), flush=True)

@@ -144,8 +144,10 @@ int matmul_tuned(const void *A, int64_t lda, const void *W, int64_t ldw, void *C
  * j % page_size.  Split s covers tokens [s*split_size, min((s+1)*split_size, L));
  * the boundaries depend on nothing but L.  Per split the kernel forms a partial
  * (max m, sum l, accumulator acc) with bf16 MFMA products and fp32 softmax;
- * a second kernel combines the ceil(L / split_size) partials with log-sum-exp
- * rescaling in ascending split order and rounds acc / l to bf16 once.  The
+ * a second kernel folds the ceil(L / split_size) partials in ascending split
+ * order with log-sum-exp rescaling (running maximum M; a partial (m, l_s, acc_s)
+ * makes M' = max(M, m), l = l 2^(M - M') + 2^(m - M') l_s, acc likewise) and
+ * rounds acc / l to bf16 once.  The
  * whole reduction tree is a function of L alone.
  *
  *  q            [rows, num_q_heads, head_dim] bf16, row stride q_row_stride
@@ -190,8 +192,9 @@ int decode_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, con
  * batch shape -- the per-batch scheduling of [P1] section 5.5 that the page
  * names as not batch-invariant: a row's split boundaries, and so its bits, move
  * with the batch.  The rule is the fastest split size measured on MI355X for
- * these kernels: 1024 tokens for batches of at most 8 rows, 512 above (capped
- * near max_kv_len).  decode_attn_tuned_split_size() returns the size it will use;
+ * these kernels: 1024 tokens for batches of at most 4 rows, 512 for at most 8,
+ * 256 above (capped near max_kv_len) -- from 9 rows on it coincides with the
+ * fixed size of decode_attn_bi's usual configuration.  decode_attn_tuned_split_size() returns the size it will use;
  * kv_lens_host (optional, may be NULL) is accepted for API symmetry.  The
  * workspace is sized with decode_attn_workspace_size(..., that split size).
  * Other arguments as decode_attn_bi.
@@ -204,6 +207,45 @@ int decode_attn_tuned(const void *q, int64_t q_row_stride, const void *k_cache,
                       int64_t out_row_stride, int64_t rows, int num_q_heads, int num_kv_heads,
                       int head_dim, int page_size, int max_kv_len, float scale, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/*
+ * prefill_attn_bi: attention of a run of consecutive prompt tokens of ONE
+ * request -- positions start_pos .. start_pos + tokens - 1, token t attending
+ * causally to the L_t = start_pos + t + 1 cache entries 0 .. start_pos + t --
+ * over the request's block-table row.  Chunked prefill and prefix caching
+ * ([P1] section 5.5 "Why Attention Is the Hardest Case", section 6.4 "A Single
+ * Request Can Break It Too"; [P3] "Where It Breaks", on prefix caching
+ * reintroducing shape dependence) need a token's reduction order not to depend on how many tokens
+ * of its sequence are processed together.  Here each (token, query head) is
+ * reduced exactly as decode_attn_bi reduces a row with that query and
+ * kv_len = L_t (same absolute split boundaries, same per-split partial, same
+ * ascending merge), so the output of token t is bit-identical to the
+ * decode_attn_bi row for it, whatever start_pos, tokens and the chunking are.
+ * Only the schedule differs: a workgroup loads each K/V page pair once and
+ * serves a block of prompt tokens from it.
+ * The chunk's K and V must already be in the cache (kv_append first).
+ *  q              [tokens, num_q_heads, head_dim] bf16, row stride q_row_stride
+ *  k_cache, v_cache  as for decode_attn_bi
+ *  block_table_row  int32 physical page ids of the request, at least
+ *                 ceil((start_pos + tokens) / page_size) entries (device)
+ *  out            [tokens, num_q_heads, head_dim] bf16, row stride out_row_stride
+ *  workspace      >= prefill_attn_workspace_size(...) bytes, 16-byte aligned; that
+ *                 size is 0 (no workspace; NULL allowed) when the chunk has enough
+ *                 tokens to fill the GPU with token blocks, otherwise the split
+ *                 partials are staged there as in decode_attn_bi (item layout
+ *                 with rows = tokens, nsmax = ceil((start_pos+tokens)/split_size))
+ * Supported: head_dim 64 or 128; page_size 16; split_size a positive multiple of
+ * page_size, at most 256 (one page pair per wave); a group of 1..16 query heads
+ * per kv head; start_pos + tokens <= 2^30; 16-byte aligned q, out and caches,
+ * row strides multiples of 8.  tokens == 0 is a no-op.
+ */
+size_t prefill_attn_workspace_size(int64_t tokens, int num_q_heads, int num_kv_heads,
+                                   int head_dim, int64_t start_pos, int split_size);
+int prefill_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, const void *v_cache,
+                    const int32_t *block_table_row, int64_t start_pos, int64_t tokens, void *out,
+                    int64_t out_row_stride, int num_q_heads, int num_kv_heads, int head_dim,
+                    int page_size, int split_size, float scale, void *workspace,
+                    size_t workspace_bytes, void *stream);
 
 /*
  * kv_append: write new tokens' K and V into their cache slots BEFORE attention

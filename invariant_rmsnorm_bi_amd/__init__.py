@@ -11,6 +11,7 @@ Entry points (see include/rbi.h for the exact contracts):
   rmsnorm_bi / rmsnorm_tuned
   matmul_bi / matmul_tuned
   decode_attn_bi / decode_attn_tuned
+  prefill_attn_bi
   kv_append, embed, residual_add, swiglu, argmax_rows
 """
 from __future__ import annotations
@@ -24,7 +25,8 @@ import torch
 __all__ = [
     "RbiError", "lib", "lib_path", "rmsnorm_bi", "rmsnorm_tuned", "matmul_bi", "matmul_tuned",
     "matmul_tuned_workspace_size", "decode_attn_bi", "decode_attn_tuned",
-    "decode_attn_workspace_size", "decode_attn_tuned_split_size", "kv_append", "embed",
+    "decode_attn_workspace_size", "decode_attn_tuned_split_size", "prefill_attn_bi",
+    "prefill_attn_workspace_size", "kv_append", "embed",
     "residual_add", "swiglu", "argmax_rows", "EXPORTS",
 ]
 
@@ -37,7 +39,8 @@ RBI_F32, RBI_BF16 = 0, 1
 EXPORTS = (
     "rbi_status_string", "rbi_abi_version", "rmsnorm_bi", "rmsnorm_tuned", "matmul_bi",
     "matmul_tuned", "matmul_tuned_workspace_size", "decode_attn_workspace_size",
-    "decode_attn_bi", "decode_attn_tuned_split_size", "decode_attn_tuned", "kv_append",
+    "decode_attn_bi", "decode_attn_tuned_split_size", "decode_attn_tuned",
+    "prefill_attn_workspace_size", "prefill_attn_bi", "kv_append",
     "rbi_embed", "rbi_residual_add", "rbi_swiglu", "rbi_argmax_rows",
 )
 
@@ -79,6 +82,9 @@ def lib() -> ctypes.CDLL:
         "decode_attn_tuned_split_size": ([i64, i32, i32, p], i32),
         "decode_attn_tuned": ([p, i64, p, p, p, i64, p, p, p, i64, i64, i32, i32, i32, i32, i32,
                                f32, p, sz, p], i32),
+        "prefill_attn_workspace_size": ([i64, i32, i32, i32, i64, i32], sz),
+        "prefill_attn_bi": ([p, i64, p, p, p, i64, i64, p, i64, i32, i32, i32, i32, i32, f32, p,
+                             sz, p], i32),
         "kv_append": ([p, i64, p, i64, p, i64, p, p, i64, i32, i32, i32, p], i32),
         "rbi_embed": ([p, i64, i64, p, i64, p, i64, p], i32),
         "rbi_residual_add": ([p, p, p, i64, p], i32),
@@ -292,6 +298,54 @@ def decode_attn_tuned(q, k_cache, v_cache, block_table, kv_lens, max_kv_len: int
                                  max_kv_len, float(scale), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream())
     _check(st, "decode_attn_tuned")
+    return out
+
+
+def prefill_attn_workspace_size(tokens: int, num_q_heads: int, num_kv_heads: int,
+                                head_dim: int, start_pos: int, split_size: int) -> int:
+    return int(lib().prefill_attn_workspace_size(tokens, num_q_heads, num_kv_heads, head_dim,
+                                                 start_pos, split_size))
+
+
+def prefill_attn_bi(q, k_cache, v_cache, block_table_row, start_pos: int,
+                    split_size: int = 256, scale: float | None = None, out=None,
+                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Attention of consecutive prompt tokens start_pos .. start_pos + len(q) - 1 of one
+    request (causal), bit-identical per token to the decode_attn_bi row with
+    kv_len = position + 1.  The chunk's K/V must already be in the cache."""
+    _need_cuda(q, k_cache, v_cache, block_table_row)
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise RbiError("q and the KV cache must be bf16")
+    if block_table_row.dtype != torch.int32 or block_table_row.dim() != 1 or \
+            not block_table_row.is_contiguous():
+        raise RbiError("block_table_row must be a contiguous int32 vector")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()) or k_cache.dim() != 4 or \
+            v_cache.shape != (k_cache.shape[0], k_cache.shape[1], k_cache.shape[3],
+                              k_cache.shape[2]):
+        raise RbiError("caches must be K [num_pages, num_kv_heads, page_size, head_dim] and "
+                       "V [num_pages, num_kv_heads, head_dim, page_size], contiguous")
+    tokens, hq, d = q.shape
+    if q.stride(2) != 1 or q.stride(1) != d:
+        raise RbiError("q must be [tokens, heads, head_dim] with packed heads")
+    _, hkv, page, d2 = k_cache.shape
+    if d2 != d:
+        raise RbiError("head_dim mismatch between q and the cache")
+    if block_table_row.shape[0] * page < start_pos + tokens:
+        raise RbiError("block_table_row does not cover start_pos + tokens")
+    if out is None:
+        out = torch.empty((tokens, hq, d), dtype=torch.bfloat16, device=q.device)
+    if out.stride(2) != 1 or out.stride(1) != d:
+        raise RbiError("out must be [tokens, heads, head_dim] with packed heads")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    need = prefill_attn_workspace_size(tokens, hq, hkv, d, start_pos, split_size)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().prefill_attn_bi(_ptr(q), _lead_stride(q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(block_table_row), start_pos, tokens, _ptr(out),
+                               _lead_stride(out), hq, hkv, d, page, split_size, float(scale),
+                               _ptr(workspace), ws_bytes, _stream())
+    _check(st, "prefill_attn_bi")
     return out
 
 

@@ -48,6 +48,24 @@ struct AttnK {
     static constexpr int DB = D / 16;       // 16-wide d blocks of the PV product
 };
 
+// 2^x on the transcendental unit (v_exp_f32).  Results below the normal range
+// may flush to zero; every use here is a softmax weight or a rescaling factor,
+// where that is immaterial, and all attention paths share this one function.
+__device__ __forceinline__ float exp2_hw(float x)
+{
+    return __builtin_amdgcn_exp2f(x);
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to packed bf16 (lo in bits 0..15), round to nearest even, by
+// the conversion instruction.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 __device__ __forceinline__ int clamp_len(int L, int max_len)
 {
     return L < 1 ? 1 : (L > max_len ? max_len : L);
@@ -55,7 +73,241 @@ __device__ __forceinline__ int clamp_len(int L, int max_len)
 
 
 
+// ---------------------------------------------------------------------------
+// The per-(token, query head) arithmetic, shared by the decode and the prefill
+// kernels so that a prompt token's result is the same bits as the decode row
+// with the same query, cache and length.
+// ---------------------------------------------------------------------------
+
+// Register image of one page pair (32 tokens) of one kv head: K as operand A of
+// the score product, V as operand B of the P.V product.
 template <int D>
+struct PairFrag {
+    uint4 k[2][AttnK<D>::KCH];
+    uint4 v[AttnK<D>::DB];
+};
+
+// Lane roles inside a wave (fixed):
+//   * lane group lg = lane / 16 owns the 8-token run lg of the pair: page slot
+//     lg / 2, in-page tokens 8 * (lg % 2) .. +7 -- its scores, P values and V loads;
+//   * score block b (one MFMA, b = 0, 1) has K row i = in-page token
+//     8 * ((i / 4) % 2) + 4b + i % 4 of slot i / 8, so output rows 4 * lg + j land
+//     in lane group lg as token 4b + j of its run;
+//   * the P.V k-step then takes each lane group's run: the lane's P values in
+//     token order, and one 16-byte run of the head-dim-major V page per d.
+struct PairLanes {
+    int lane;
+    __device__ __forceinline__ explicit PairLanes(int l) : lane(l) {}
+    __device__ __forceinline__ int lr() const { return lane & 15; }
+    __device__ __forceinline__ int lg() const { return lane >> 4; }
+    __device__ __forceinline__ int kslot() const { return (lane & 15) >> 3; }     // K row's page slot
+    __device__ __forceinline__ int krow() const { return 8 * ((lane >> 2) & 1) + (lane & 3); }
+    __device__ __forceinline__ int vslot() const { return lane >> 5; }           // run's page slot
+    __device__ __forceinline__ int vrun() const { return 8 * ((lane >> 4) & 1); }  // run's first token
+};
+
+// Loads page pair pr of a split whose first valid_pages pages have their
+// physical ids in lanes 0 .. of my_page.  A page slot past the last valid page
+// reads that page again (masked later), so no load is conditional.
+template <int D>
+__device__ __forceinline__ void load_pair(PairFrag<D> &f, int pr, int my_page, int valid_pages,
+                                          const uint16_t *__restrict__ k_cache,
+                                          const uint16_t *__restrict__ v_cache, int hkv, int g,
+                                          const PairLanes &ln)
+{
+    using P = AttnK<D>;
+    const int64_t kphys = __shfl(my_page, min(2 * pr + ln.kslot(), valid_pages - 1), kWave);
+    const int64_t vphys = __shfl(my_page, min(2 * pr + ln.vslot(), valid_pages - 1), kWave);
+    const uint16_t *kp = k_cache + ((kphys * hkv + g) * PAGE + ln.krow()) * D + ln.lg() * P::DPL;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int cc = 0; cc < P::KCH; ++cc)
+            f.k[b][cc] = *reinterpret_cast<const uint4 *>(kp + 4 * b * D + 8 * cc);
+    const uint16_t *vp = v_cache + ((vphys * hkv + g) * D + ln.lr()) * PAGE + ln.vrun();
+#pragma unroll
+    for (int db = 0; db < P::DB; ++db)
+        f.v[db] = *reinterpret_cast<const uint4 *>(vp + 16 * db * PAGE);
+}
+
+// Live tokens of this lane group's run in page pair pr of the split [t0, t1)
+// (valid_pages = ceil((t1 - t0) / PAGE)).
+__device__ __forceinline__ int run_keep(int pr, int t0, int t1, int valid_pages,
+                                        const PairLanes &ln)
+{
+    const int first = t0 + (2 * pr + ln.vslot()) * PAGE + ln.vrun();
+    return (2 * pr + ln.vslot() < valid_pages) ? max(0, min(8, t1 - first)) : 0;
+}
+
+// V entries of tokens past `keep` in this lane group's run, set to exact zeros
+// (their weights are 0, but a stale non-finite value times 0 would not be 0).
+template <int D>
+__device__ __forceinline__ void mask_runs(const uint4 (&src)[AttnK<D>::DB], int keep,
+                                          uint4 (&dst)[AttnK<D>::DB])
+{
+    uint32_t vmask[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        vmask[i] = (2 * i < keep ? 0x0000ffffu : 0u) | (2 * i + 1 < keep ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int db = 0; db < AttnK<D>::DB; ++db)
+        dst[db] = make_uint4(src[db].x & vmask[0], src[db].y & vmask[1], src[db].z & vmask[2],
+                             src[db].w & vmask[3]);
+}
+
+// One page pair folded into the wave's running (m, l, acc) for the 16 query rows
+// at qt (LDS, [16][D]), with K from f and V from v (already masked by mask_runs
+// unless the pair is full).  Tokens past `keep` in a run get weight 0.
+//   scores  s2 = (K . q) * scale * log2(e), fp32, -inf when masked
+//   m_new   = max(m_run, max_j s2_j)           (per head, over the 32 tokens)
+//   p_j     = bf16(2^(s2_j - m_new))
+//   l_run   = fma(l_run, 2^(m_run - m_new), sum of this lane's p_j in token order)
+//   acc     = acc * 2^(m_run - m_new) + P . V  (bf16 MFMA, fp32 accumulate)
+// FRESH: the state is the initial (-inf, 0, 0), for which the rescaling is the
+// identity on zeros and is skipped (same bits).  full: every token of the pair
+// is live (keep = 8 in every run), so the score mask is all-pass and skipped.
+template <int D, bool FRESH>
+__device__ __forceinline__ void pair_update(const PairFrag<D> &f, const uint4 (&v)[AttnK<D>::DB],
+                                            int keep, bool full, const uint16_t *__restrict__ qt,
+                                            float scale_log2, const PairLanes &ln, float &m_run,
+                                            float &l_run, f32x4_t (&acc)[AttnK<D>::DB])
+{
+    using P = AttnK<D>;
+    // scores: lane holds head lr, token 4b + j of its run
+    float sv[2][4];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < P::KCH; ++cc) {
+            const bf16x8_t qf = as_bf16x8(
+                *reinterpret_cast<const uint4 *>(qt + ln.lr() * D + ln.lg() * P::DPL + 8 * cc));
+            sc = mfma_16x16x32_bf16(as_bf16x8(f.k[b][cc]), qf, sc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float v = (full || 4 * b + j < keep) ? sc[j] * scale_log2 : -INFINITY;
+            sv[b][j] = v;
+            mloc = fmaxf(mloc, v);
+        }
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+    const float m_new = FRESH ? mloc : fmaxf(m_run, mloc);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+
+    uint32_t pw[2][2];  // bf16 p, two per word, token order within the run
+    float psum = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+            const uint32_t w =
+                cvt_pk_bf16(exp2_hw(sv[b][j] - m_use), exp2_hw(sv[b][j + 1] - m_use));
+            psum += __uint_as_float(w << 16);
+            psum += __uint_as_float(w & 0xffff0000u);
+            pw[b][j / 2] = w;
+        }
+    }
+    if constexpr (FRESH) {
+        l_run = psum;
+    } else {
+        const float alpha = exp2_hw(m_run - m_use);
+        l_run = fmaf(l_run, alpha, psum);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float aj = __shfl(alpha, 4 * ln.lg() + j, kWave);
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db)
+                acc[db][j] *= aj;
+        }
+    }
+    m_run = m_new;
+
+    const bf16x8_t pf = as_bf16x8(make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
+#pragma unroll
+    for (int db = 0; db < P::DB; ++db)
+        acc[db] = mfma_16x16x32_bf16(pf, as_bf16x8(v[db]), acc[db]);
+}
+
+// True when page pair pr of the split [t0, t1) is live in every token.
+__device__ __forceinline__ bool pair_full(int pr, int t0, int t1)
+{
+    return t0 + (2 * pr + 2) * PAGE <= t1;
+}
+
+// A wave's (m, l, acc) into the workgroup's combine buffers; l is the wave's
+// sum for head lr over the four lane groups in butterfly order.
+template <int D>
+__device__ __forceinline__ void stash_wave(float m_run, float l_run,
+                                           const f32x4_t (&acc)[AttnK<D>::DB], int wave,
+                                           const PairLanes &ln, float (*c_m)[16],
+                                           float (*c_l)[16], float (*c_acc)[16][D])
+{
+    float l_w = l_run;
+    l_w += __shfl_xor(l_w, 16, kWave);
+    l_w += __shfl_xor(l_w, 32, kWave);
+    if (ln.lg() == 0) {
+        c_m[wave][ln.lr()] = m_run;
+        c_l[wave][ln.lr()] = l_w;
+    }
+#pragma unroll
+    for (int db = 0; db < AttnK<D>::DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            c_acc[wave][4 * ln.lg() + j][16 * db + ln.lr()] = acc[db][j];
+}
+
+// The split's partial for head h from the waves' stashes, in wave order
+// 0 .. WAVES-1:  M = max_w m_w, c_w = 2^(m_w - M) (0 for an idle wave),
+// l = fma(c_w, l_w, l) and acc = fma(c_w, acc_w, acc) over w, starting from 0,
+// for the EPT elements at dq.
+template <int D>
+__device__ __forceinline__ void combine_ml(const float (*c_m)[16], const float (*c_l)[16], int h,
+                                           float &M, float &l, float (&cw)[WAVES])
+{
+    float mw[WAVES];
+    M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+        mw[w] = c_m[w][h];
+        M = fmaxf(M, mw[w]);
+    }
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w)
+        cw[w] = (mw[w] == -INFINITY) ? 0.f : exp2_hw(mw[w] - M);
+    l = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w)
+        l = fmaf(cw[w], c_l[w][h], l);
+}
+
+template <int D, int EPT>
+__device__ __forceinline__ void combine_acc(const float (*c_acc)[16][D], const float (&cw)[WAVES],
+                                            int h, int dq, float (&o)[EPT])
+{
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        float a = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w)
+            a = fmaf(cw[w], c_acc[w][h][dq + e], a);
+        o[e] = a;
+    }
+}
+
+// Ascending fold of split partials (the merge): with M the largest partial
+// maximum folded so far (-inf before the first), a new partial (m, l_s, a_s)
+// gives M' = max(M, m), al = 2^(M - M'), be = 2^(m - M'),
+// l = fma(be, l_s, l * al) and o = fma(be, a_s, o * al).
+__device__ __forceinline__ float fold_step(float acc, float al, float be, float x)
+{
+    return fmaf(be, x, acc * al);
+}
+
+// MULTI: splits longer than 2 * PAGE * WAVES tokens (several page pairs per wave).
+template <int D, bool MULTI>
 __global__ __launch_bounds__(512, 4) void attn_split_kernel(
     const uint16_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_table,
@@ -71,7 +323,7 @@ __global__ __launch_bounds__(512, 4) void attn_split_kernel(
     const int s = blockIdx.x, g = blockIdx.y;
     const int64_t r = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
+    const PairLanes ln(lane);
     // The split's block-table entries (up to 64, one per lane) are read before the
     // length is known, so that this read and the length read overlap; the index is
     // clamped into the table row (ceil(max_kv_len / 16) entries, checked by the
@@ -97,43 +349,12 @@ __global__ __launch_bounds__(512, 4) void attn_split_kernel(
         acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // Wave w takes the page pairs 2w, 2w+1 (+ 2*WAVES*i for splits longer than
-    // 2*WAVES pages), one pair per step.  Within a step:
-    //   * lane group lg owns the 8-token run lg: page slot lg/2, in-page tokens
-    //     8*(lg%2) .. +7 -- its scores, its P values and its V loads;
-    //   * score block b (one MFMA, b = 0, 1) has K row i = in-page token
-    //     8*((i/4)%2) + 4b + i%4 of slot i/8, so output rows 4*lg + j land in lane
-    //     group lg as token 4b + j of its run;
-    //   * the P.V k-step then takes each lane group's run: the lane's P values in
-    //     token order, and one 16-byte run of the head-dim-major V page per d.
-    // A page slot past the split's last page reads that last page again and is
-    // masked afterwards, so no load is conditional.
-    const int kslot = lr >> 3;                              // K row's page slot
-    const int krow = 8 * ((lr >> 2) & 1) + (lr & 3);        // K row's in-page token (b = 0)
-    const int vslot = lg >> 1, vrun = 8 * (lg & 1);         // this lane group's run
+    // 2*WAVES pages), one pair per step.
     const int pairs = (valid_pages + 1) / 2;
-
-    struct StepData {
-        uint4 k[2][P::KCH];
-        uint4 v[P::DB];
-    };
-    auto load_step = [&](int pr, StepData &sd) {
-        const int64_t kphys = __shfl(my_page, min(2 * pr + kslot, valid_pages - 1), kWave);
-        const int64_t vphys = __shfl(my_page, min(2 * pr + vslot, valid_pages - 1), kWave);
-        const uint16_t *kp = k_cache + ((kphys * hkv + g) * PAGE + krow) * D + lg * P::DPL;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int cc = 0; cc < P::KCH; ++cc)
-                sd.k[b][cc] = *reinterpret_cast<const uint4 *>(kp + 4 * b * D + 8 * cc);
-        const uint16_t *vp = v_cache + ((vphys * hkv + g) * D + lr) * PAGE + vrun;
-#pragma unroll
-        for (int db = 0; db < P::DB; ++db)
-            sd.v[db] = *reinterpret_cast<const uint4 *>(vp + 16 * db * PAGE);
-    };
     // first step's loads go out before the query is staged
-    StepData sd;
+    PairFrag<D> f;
     if (wave < pairs)
-        load_step(wave, sd);
+        load_pair<D>(f, wave, my_page, valid_pages, k_cache, v_cache, hkv, g, ln);
 
     // the group's query rows, staged once in LDS (rows past the group are zero)
     for (int i = threadIdx.x; i < 16 * D / 8; i += WAVES * 64) {
@@ -144,124 +365,44 @@ __global__ __launch_bounds__(512, 4) void attn_split_kernel(
     }
     __syncthreads();  // q_lds ready
 
-    for (int pr = wave; pr < pairs; pr += WAVES) {
-        if (pr != wave)
-            load_step(pr, sd);
-        uint4(&kd)[2][P::KCH] = sd.k;
-        uint4(&vd)[P::DB] = sd.v;
-
-        // live tokens of this lane group's run; the others get weight 0 and their V
-        // entries exact zeros (a stale non-finite value times 0 would not be 0)
-        const int first = t0 + (2 * pr + vslot) * PAGE + vrun;
-        const int keep = (2 * pr + vslot < valid_pages) ? max(0, min(8, t1 - first)) : 0;
-        uint32_t vmask[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            vmask[i] = (2 * i < keep ? 0x0000ffffu : 0u) | (2 * i + 1 < keep ? 0xffff0000u : 0u);
-#pragma unroll
-        for (int db = 0; db < P::DB; ++db)
-            vd[db] = make_uint4(vd[db].x & vmask[0], vd[db].y & vmask[1], vd[db].z & vmask[2],
-                                vd[db].w & vmask[3]);
-
-        // scores: lane holds head lr, token 4b + j of its run
-        float sv[2][4];
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int cc = 0; cc < P::KCH; ++cc) {
-                const bf16x8_t qf = as_bf16x8(
-                    *reinterpret_cast<const uint4 *>(&q_lds[lr][lg * P::DPL + 8 * cc]));
-                sc = mfma_16x16x32_bf16(as_bf16x8(kd[b][cc]), qf, sc);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float v = (4 * b + j < keep) ? sc[j] * scale_log2 : -INFINITY;
-                sv[b][j] = v;
-                mloc = fmaxf(mloc, v);
-            }
+    if constexpr (!MULTI) {
+        if (wave < pairs) {
+            const int keep = run_keep(wave, t0, t1, valid_pages, ln);
+            const bool full = pair_full(wave, t0, t1);
+            if (!full)
+                mask_runs<D>(f.v, keep, f.v);
+            pair_update<D, true>(f, f.v, keep, full, &q_lds[0][0], scale_log2, ln, m_run, l_run,
+                                 acc);
         }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-        const float m_new = fmaxf(m_run, mloc);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
-
-        uint32_t pw[2][2];  // bf16 p, two per word, token order within the run
-        float psum = 0.f;
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            uint32_t e[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                e[j] = f32_to_bf16(exp2f(sv[b][j] - m_use));
-                psum += bf16_to_f32(e[j]);
-            }
-            pw[b][0] = e[0] | (e[1] << 16);
-            pw[b][1] = e[2] | (e[3] << 16);
+    } else {
+        // (register budget: the query fragments are re-read from LDS every pair --
+        // the empty asm keeps them from being hoisted out of the loop -- and the
+        // all-pass mask of a full pair is applied anyway, which gives the same bits)
+        for (int pr = wave; pr < pairs; pr += WAVES) {
+            asm volatile("" ::: "memory");
+            if (pr != wave)
+                load_pair<D>(f, pr, my_page, valid_pages, k_cache, v_cache, hkv, g, ln);
+            const int keep = run_keep(pr, t0, t1, valid_pages, ln);
+            mask_runs<D>(f.v, keep, f.v);
+            pair_update<D, false>(f, f.v, keep, false, &q_lds[0][0], scale_log2, ln, m_run, l_run,
+                                  acc);
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float aj = __shfl(alpha, 4 * lg + j, kWave);
-#pragma unroll
-            for (int db = 0; db < P::DB; ++db)
-                acc[db][j] *= aj;
-        }
-        const bf16x8_t pf = as_bf16x8(make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
-#pragma unroll
-        for (int db = 0; db < P::DB; ++db)
-            acc[db] = mfma_16x16x32_bf16(pf, as_bf16x8(vd[db]), acc[db]);
     }
 
-    // this wave's sum for head lr: the four lane groups in butterfly order
-    float l_w = l_run;
-    l_w += __shfl_xor(l_w, 16, kWave);
-    l_w += __shfl_xor(l_w, 32, kWave);
-    if (lg == 0) {
-        c_m[wave][lr] = m_run;
-        c_l[wave][lr] = l_w;
-    }
-#pragma unroll
-    for (int db = 0; db < P::DB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            c_acc[wave][4 * lg + j][16 * db + lr] = acc[db][j];
+    stash_wave<D>(m_run, l_run, acc, wave, ln, c_m, c_l, c_acc);
     __syncthreads();
 
-    // combine the waves in order 0 .. WAVES-1; thread t: head t / 32, d slice
-    const int h = threadIdx.x >> 5;
-    const int dq = (threadIdx.x & 31) * (D / 32);
+    // combine the waves; thread t: head t / 32, d slice
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-    float mw[WAVES], M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-        mw[w] = c_m[w][h];
-        M = fmaxf(M, mw[w]);
-    }
-    float cw[WAVES];
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w)
-        cw[w] = (mw[w] == -INFINITY) ? 0.f : exp2f(mw[w] - M);
-    float l = 0.f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w)
-        l = l + cw[w] * c_l[w][h];
+    constexpr int EPT = D / 32;  // elements of the head row this thread owns
+    const int h = threadIdx.x >> 5;
+    const int dq = (threadIdx.x & 31) * EPT;
+    float M, l, cw[WAVES];
+    combine_ml<D>(c_m, c_l, h, M, l, cw);
     if (h < G) {
         const int64_t item = (r * hq + g * G + h) * nsmax + s;
-        constexpr int EPT = D / 32;  // elements of the head row this thread owns
         float o[EPT];
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            float a = 0.f;
-#pragma unroll
-            for (int w = 0; w < WAVES; ++w)
-                a = a + cw[w] * c_acc[w][h][dq + e];
-            o[e] = a;
-        }
+        combine_acc<D, EPT>(c_acc, cw, h, dq, o);
         float *dst = ws_acc + item * D + dq;
         if constexpr (EPT == 4)
             *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
@@ -274,15 +415,17 @@ __global__ __launch_bounds__(512, 4) void attn_split_kernel(
     }
 }
 
-// One wave per (row, query head): ordered combine of the row's split partials.
-// The maximum is taken lane-parallel (exact, so order-free); the scale factors
-// 2^(m_s - M) are formed lane-parallel, one split per lane; the sums over splits
-// run in ascending split order in every lane.
+// One wave per (row, query head): the ascending fold of the row's split
+// partials.  The running maxima (prefix maxima over the splits, exact, so
+// order-free) and the factors al, be of each split are formed lane-parallel,
+// one split per lane; the fold itself runs in ascending split order in every
+// lane.  Row r's length is kv_lens[r], or start + r + 1 when kv_lens is null
+// (consecutive prompt tokens).
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(
     const float *__restrict__ ws_acc, const float *__restrict__ ws_ml,
-    const int32_t *__restrict__ kv_lens, int64_t rows, int hq, int S, int max_kv_len, int nsmax,
-    uint16_t *__restrict__ out, int64_t out_row_stride)
+    const int32_t *__restrict__ kv_lens, int start, int64_t rows, int hq, int S, int max_kv_len,
+    int nsmax, uint16_t *__restrict__ out, int64_t out_row_stride)
 {
     constexpr int EPL = D / 64;  // elements per lane
     constexpr int UNROLL = 8;
@@ -292,24 +435,33 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
         return;
     const int64_t r = item / hq;
     const int h = (int)(item % hq);
-    const int L = clamp_len(kv_lens[r], max_kv_len);
+    const int L = kv_lens ? clamp_len(kv_lens[r], max_kv_len) : start + (int)r + 1;
     const int n = (L + S - 1) / S;  // splits of this row
     const float *ml = ws_ml + item * nsmax * 2;
     const float *ac = ws_acc + item * nsmax * D + lane * EPL;
-    float M = -INFINITY;
-    for (int s = lane; s < n; s += 64)
-        M = fmaxf(M, ml[2 * s]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        M = fmaxf(M, __shfl_xor(M, off, kWave));
+    float M = -INFINITY;  // running maximum, the same in every lane
     float l = 0.f, o[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
         o[e] = 0.f;
     for (int s0 = 0; s0 < n; s0 += 64) {
         const int sl = s0 + lane;
-        const float c_l = sl < n ? exp2f(ml[2 * sl] - M) : 0.f;
+        const float m_l = sl < n ? ml[2 * sl] : -INFINITY;
         const float l_l = sl < n ? ml[2 * sl + 1] : 0.f;
+        float Mi = m_l;  // max(M, m_s0 .. m_sl)
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float t = __shfl_up(Mi, off, kWave);
+            if (lane >= off)
+                Mi = fmaxf(Mi, t);
+        }
+        Mi = fmaxf(Mi, M);
+        float Mp = __shfl_up(Mi, 1, kWave);  // the maximum before split sl
+        if (lane == 0)
+            Mp = M;
+        const float al_l = exp2_hw(Mp - Mi);
+        const float be_l = exp2_hw(m_l - Mi);
+        M = __shfl(Mi, 63, kWave);
         const int cnt = min(64, n - s0);
         for (int j0 = 0; j0 < cnt; j0 += UNROLL) {
             float a[UNROLL][EPL];
@@ -321,11 +473,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 if (j0 + u < cnt) {
-                    const float c = __shfl(c_l, j0 + u, kWave);
-                    l = l + c * __shfl(l_l, j0 + u, kWave);
+                    const float al = __shfl(al_l, j0 + u, kWave);
+                    const float be = __shfl(be_l, j0 + u, kWave);
+                    l = fold_step(l, al, be, __shfl(l_l, j0 + u, kWave));
 #pragma unroll
                     for (int e = 0; e < EPL; ++e)
-                        o[e] = o[e] + c * a[u][e];
+                        o[e] = fold_step(o[e], al, be, a[u][e]);
                 }
             }
         }
@@ -335,6 +488,156 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
         *reinterpret_cast<uint32_t *>(dst) = pack_bf16x2(o[0] / l, o[1] / l);
     } else {
         dst[0] = (uint16_t)f32_to_bf16(o[0] / l);
+    }
+}
+
+// Prefill: one request's consecutive prompt tokens start .. start + tokens - 1,
+// token t with causal length L_t = start + t + 1, over one block-table row.
+// Each (token, query head) goes through exactly the decode arithmetic above --
+// the same split boundaries, the same page pairs per wave, the same wave
+// combine and the same ascending fold -- so its bits are those of the decode
+// row with that query and length.  What changes is the schedule: a workgroup
+// takes TG consecutive tokens of one kv head, loads each page pair of a split
+// once into its waves' registers and runs every token of the block against it.
+//   FUSED:  grid (token blocks, kv heads); the workgroup walks the splits in
+//           ascending order and folds each token's split partials as they are
+//           formed, in the registers of the combining threads; no workspace.
+//   !FUSED: grid (splits, kv heads, token blocks); each workgroup writes its
+//           tokens' partials of one split to the workspace (item layout of the
+//           decode kernel) and the merge kernel folds them.  For short chunks
+//           after a long prefix, where token blocks alone cannot fill the chip.
+// Split sizes up to 2 * PAGE * WAVES = 256 tokens (one page pair per wave).
+template <int D, int TG, bool FUSED>
+__global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
+    const uint16_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ k_cache,
+    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ btrow, int start, int tokens,
+    int hq, int hkv, int S, float scale_log2, uint16_t *__restrict__ out, int64_t out_row_stride,
+    int nsmax, float *__restrict__ ws_acc, float *__restrict__ ws_ml)
+{
+    using P = AttnK<D>;
+    static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+    constexpr int EPT = D / 32;
+    __shared__ __attribute__((aligned(16))) uint16_t q_lds[TG][16][D];
+    __shared__ float c_m[WAVES][16], c_l[WAVES][16];
+    __shared__ __attribute__((aligned(16))) float c_acc[WAVES][16][D];
+
+    const int nblk = FUSED ? gridDim.x : gridDim.z;
+    // the blocks with the longest lengths (the most splits) are dispatched first
+    const int blk = nblk - 1 - (FUSED ? blockIdx.x : blockIdx.z);
+    const int g = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const PairLanes ln(lane);
+    const int G = hq / hkv;
+    const int tok0 = blk * TG;
+    const int tcount = min(TG, tokens - tok0);
+    const int Lmax = start + tok0 + tcount;  // the block's longest length
+    const int split_pages = S / PAGE;
+    const int row_pages = (start + tokens + PAGE - 1) / PAGE;
+    const int s_first = FUSED ? 0 : blockIdx.x;
+    const int s_end = FUSED ? (Lmax + S - 1) / S : min((int)blockIdx.x + 1, (Lmax + S - 1) / S);
+    if (s_first >= s_end)
+        return;
+
+    for (int i = threadIdx.x; i < TG * 16 * D / 8; i += WAVES * 64) {
+        const int t = i / (16 * D / 8), hh = (i / (D / 8)) % 16, c = i % (D / 8);
+        *reinterpret_cast<uint4 *>(&q_lds[t][hh][8 * c]) =
+            (t < tcount && hh < G)
+                ? *reinterpret_cast<const uint4 *>(q + (int64_t)(tok0 + t) * q_row_stride +
+                                                   (int64_t)(g * G + hh) * D + 8 * c)
+                : make_uint4(0, 0, 0, 0);
+    }
+
+    const int h = threadIdx.x >> 5;  // combining thread: head h, elements dq .. dq + EPT - 1
+    const int dq = (threadIdx.x & 31) * EPT;
+    float Mt[TG], lt[TG], ot[TG][EPT];  // FUSED: each token's fold so far
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+        Mt[t] = -INFINITY;
+        lt[t] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+            ot[t][e] = 0.f;
+    }
+
+    for (int s = s_first; s < s_end; ++s) {
+        const int t0 = s * S;
+        const int vp_blk = (min(t0 + S, Lmax) - t0 + PAGE - 1) / PAGE;
+        const int my_page = btrow[min(s * split_pages + min(lane, split_pages - 1), row_pages - 1)];
+        PairFrag<D> f;
+        if (wave < (vp_blk + 1) / 2)
+            load_pair<D>(f, wave, my_page, vp_blk, k_cache, v_cache, hkv, g, ln);
+        __syncthreads();  // q_lds staged (first split); the previous split's combine done
+#pragma unroll
+        for (int t = 0; t < TG; ++t) {
+            const int Lt = start + tok0 + t + 1;
+            if (t >= tcount || t0 >= Lt)  // the same for the whole workgroup
+                continue;
+            const int t1 = min(t0 + S, Lt);
+            const int vp = (t1 - t0 + PAGE - 1) / PAGE;
+            float m_run = -INFINITY, l_run = 0.f;
+            f32x4_t acc[P::DB];
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db)
+                acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (wave < (vp + 1) / 2) {
+                const int keep = run_keep(wave, t0, t1, vp, ln);
+                if (pair_full(wave, t0, t1)) {
+                    pair_update<D, true>(f, f.v, keep, true, &q_lds[t][0][0], scale_log2, ln,
+                                         m_run, l_run, acc);
+                } else {  // a masked copy: the block's V image serves every token
+                    uint4 vm[P::DB];
+                    mask_runs<D>(f.v, keep, vm);
+                    pair_update<D, true>(f, vm, keep, false, &q_lds[t][0][0], scale_log2, ln,
+                                         m_run, l_run, acc);
+                }
+            }
+            stash_wave<D>(m_run, l_run, acc, wave, ln, c_m, c_l, c_acc);
+            __syncthreads();
+            float Ms, ls, cw[WAVES];
+            combine_ml<D>(c_m, c_l, h, Ms, ls, cw);
+            if (h < G) {
+                float os[EPT];
+                combine_acc<D, EPT>(c_acc, cw, h, dq, os);
+                if constexpr (FUSED) {
+                    const float Mn = fmaxf(Mt[t], Ms);
+                    const float al = exp2_hw(Mt[t] - Mn), be = exp2_hw(Ms - Mn);
+                    lt[t] = fold_step(lt[t], al, be, ls);
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e)
+                        ot[t][e] = fold_step(ot[t][e], al, be, os[e]);
+                    Mt[t] = Mn;
+                } else {
+                    const int64_t item = ((int64_t)(tok0 + t) * hq + g * G + h) * nsmax + s;
+                    float *dst = ws_acc + item * D + dq;
+                    if constexpr (EPT == 4)
+                        *reinterpret_cast<float4 *>(dst) = make_float4(os[0], os[1], os[2], os[3]);
+                    else
+                        *reinterpret_cast<float2 *>(dst) = make_float2(os[0], os[1]);
+                    if ((threadIdx.x & 31) == 0) {
+                        ws_ml[item * 2] = Ms;
+                        ws_ml[item * 2 + 1] = ls;
+                    }
+                }
+            }
+            __syncthreads();  // the stash is reused by the next token
+        }
+    }
+
+    if constexpr (FUSED) {
+        if (h < G) {
+#pragma unroll
+            for (int t = 0; t < TG; ++t) {
+                if (t < tcount) {
+                    uint16_t *dst = out + (int64_t)(tok0 + t) * out_row_stride + (int64_t)(g * G + h) * D + dq;
+                    if constexpr (EPT == 4)
+                        *reinterpret_cast<uint2 *>(dst) =
+                            make_uint2(pack_bf16x2(ot[t][0] / lt[t], ot[t][1] / lt[t]),
+                                       pack_bf16x2(ot[t][2] / lt[t], ot[t][3] / lt[t]));
+                    else
+                        *reinterpret_cast<uint32_t *>(dst) = pack_bf16x2(ot[t][0] / lt[t], ot[t][1] / lt[t]);
+                }
+            }
+        }
     }
 }
 
@@ -375,16 +678,63 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t s)
     float *ws_ml = a.ws + a.rows * a.hq * (int64_t)nsmax * D;
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const dim3 g1((unsigned)nsmax, (unsigned)a.hkv, (unsigned)a.rows), b1(WAVES * 64);
-    attn_split_kernel<D><<<g1, b1, 0, s>>>(a.q, a.q_row_stride, a.k_cache, a.v_cache,
-                                           a.block_table, a.bt_stride, a.kv_lens, a.hq, a.hkv,
-                                           a.split, a.max_kv_len, nsmax, scale_log2, ws_acc, ws_ml);
+    if (a.split <= 2 * PAGE * WAVES)
+        attn_split_kernel<D, false><<<g1, b1, 0, s>>>(
+            a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table, a.bt_stride, a.kv_lens,
+            a.hq, a.hkv, a.split, a.max_kv_len, nsmax, scale_log2, ws_acc, ws_ml);
+    else
+        attn_split_kernel<D, true><<<g1, b1, 0, s>>>(
+            a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table, a.bt_stride, a.kv_lens,
+            a.hq, a.hkv, a.split, a.max_kv_len, nsmax, scale_log2, ws_acc, ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     const int64_t items = a.rows * a.hq;
     const dim3 g2((unsigned)((items + 3) / 4)), b2(256);
-    attn_merge_kernel<D><<<g2, b2, 0, s>>>(ws_acc, ws_ml, a.kv_lens, a.rows, a.hq, a.split,
+    attn_merge_kernel<D><<<g2, b2, 0, s>>>(ws_acc, ws_ml, a.kv_lens, 0, a.rows, a.hq, a.split,
                                            a.max_kv_len, nsmax, a.out, a.out_row_stride);
+    return hipGetLastError();
+}
+
+constexpr int kPrefillTG = 8;  // prompt tokens per prefill workgroup
+
+// The fused prefill schedule needs enough token blocks to occupy the chip (one
+// workgroup per compute unit); short chunks use the split schedule.
+bool prefill_fused(int64_t tokens, int hkv)
+{
+    const int64_t blocks = (tokens + kPrefillTG - 1) / kPrefillTG;
+    return blocks * hkv >= 256;
+}
+
+template <int D>
+hipError_t launch_prefill_d(const PrefillArgs &a, hipStream_t s)
+{
+    constexpr int TG = kPrefillTG;
+    const int nblk = (int)((a.tokens + TG - 1) / TG);
+    const int nsmax = (int)((a.start + a.tokens + a.split - 1) / a.split);
+    const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+    const dim3 blk(WAVES * 64);
+    if (prefill_fused(a.tokens, a.hkv)) {
+        attn_prefill_kernel<D, TG, true><<<dim3((unsigned)nblk, (unsigned)a.hkv), blk, 0, s>>>(
+            a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table_row, (int)a.start,
+            (int)a.tokens, a.hq, a.hkv, a.split, scale_log2, a.out, a.out_row_stride, nsmax,
+            nullptr, nullptr);
+        return hipGetLastError();
+    }
+    float *ws_acc = a.ws;
+    float *ws_ml = a.ws + a.tokens * a.hq * (int64_t)nsmax * D;
+    attn_prefill_kernel<D, TG, false>
+        <<<dim3((unsigned)nsmax, (unsigned)a.hkv, (unsigned)nblk), blk, 0, s>>>(
+            a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table_row, (int)a.start,
+            (int)a.tokens, a.hq, a.hkv, a.split, scale_log2, a.out, a.out_row_stride, nsmax,
+            ws_acc, ws_ml);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t items = a.tokens * a.hq;
+    attn_merge_kernel<D><<<dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s>>>(
+        ws_acc, ws_ml, nullptr, (int)a.start, a.tokens, a.hq, a.split,
+        (int)(a.start + a.tokens), nsmax, a.out, a.out_row_stride);
     return hipGetLastError();
 }
 
@@ -399,6 +749,19 @@ size_t attn_workspace_bytes(int64_t rows, int hq, int d, int max_kv_len, int spl
 hipError_t launch_decode_attn(const AttnArgs &a, hipStream_t s)
 {
     return a.d == 128 ? launch_attn_d<128>(a, s) : launch_attn_d<64>(a, s);
+}
+
+size_t prefill_workspace_bytes(int64_t tokens, int hq, int hkv, int d, int64_t start, int split)
+{
+    if (prefill_fused(tokens, hkv))
+        return 0;
+    const int64_t nsmax = (start + tokens + split - 1) / split;
+    return (size_t)(tokens * hq * nsmax) * (size_t)(d + 2) * sizeof(float);
+}
+
+hipError_t launch_prefill_attn(const PrefillArgs &a, hipStream_t s)
+{
+    return a.d == 128 ? launch_prefill_d<128>(a, s) : launch_prefill_d<64>(a, s);
 }
 
 hipError_t launch_kv_append(const uint16_t *k_new, int64_t ks, const uint16_t *v_new, int64_t vs,

@@ -215,12 +215,62 @@ int decode_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, con
                        split_size, max_kv_len, scale, workspace, workspace_bytes, stream);
 }
 
+size_t prefill_attn_workspace_size(int64_t tokens, int num_q_heads, int num_kv_heads,
+                                   int head_dim, int64_t start_pos, int split_size)
+{
+    if (tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        start_pos < 0 || split_size <= 0)
+        return 0;
+    return rbi::prefill_workspace_bytes(tokens, num_q_heads, num_kv_heads, head_dim, start_pos,
+                                        split_size);
+}
+
+int prefill_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, const void *v_cache,
+                    const int32_t *block_table_row, int64_t start_pos, int64_t tokens, void *out,
+                    int64_t out_row_stride, int num_q_heads, int num_kv_heads, int head_dim,
+                    int page_size, int split_size, float scale, void *workspace,
+                    size_t workspace_bytes, void *stream)
+{
+    const int hq = num_q_heads, hkv = num_kv_heads, d = head_dim;
+    if (tokens < 0 || start_pos < 0 || hq < 1 || hkv < 1 || split_size < 1 || page_size < 1)
+        return RBI_EINVAL;
+    if (hq % hkv)
+        return RBI_EINVAL;
+    if (d != 64 && d != 128)
+        return RBI_EUNSUPPORTED;
+    if (page_size != 16 || split_size % page_size || split_size > 256)
+        return RBI_EUNSUPPORTED;
+    if (hq / hkv > 16)
+        return RBI_EUNSUPPORTED;
+    if (tokens == 0)
+        return RBI_OK;
+    if (!q || !k_cache || !v_cache || !block_table_row || !out)
+        return RBI_EINVAL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return RBI_EINVAL;
+    if (q_row_stride < (int64_t)hq * d || out_row_stride < (int64_t)hq * d || q_row_stride % 8 ||
+        out_row_stride % 8)
+        return RBI_EINVAL;
+    if (start_pos + tokens > ((int64_t)1 << 30) || hkv > kGridYZ)
+        return RBI_EUNSUPPORTED;
+    const size_t need =
+        rbi::prefill_workspace_bytes(tokens, hq, hkv, d, start_pos, split_size);
+    if (need && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return RBI_EWORKSPACE;
+    const rbi::PrefillArgs a{(const uint16_t *)q, q_row_stride, (const uint16_t *)k_cache,
+                             (const uint16_t *)v_cache, block_table_row, start_pos, tokens,
+                             (uint16_t *)out, out_row_stride, hq, hkv, d, page_size, split_size,
+                             scale, (float *)workspace};
+    return launched(rbi::launch_prefill_attn(a, stream_of(stream)));
+}
+
 // Split size of the twin, tuned to the batch: the fastest split size measured on
 // MI355X for the kernels here (decode batches of 64 query / 4 kv heads, d128,
-// lengths up to 32768): 1024 tokens while the batch has at most 8 rows (fewer,
-// longer splits: less partial traffic, every wave busy), 512 beyond.  Clamped to
-// max_kv_len rounded up to the page.  The host lengths are accepted for API
-// symmetry; the rule does not need them.
+// lengths up to 32768): 1024 tokens for at most 4 rows, 512 for at most 8 (few
+// rows: fewer, longer splits leave less partial traffic and keep every wave
+// busy), 256 beyond (one page pair per wave: the leanest kernel, and enough
+// workgroups).  Clamped to max_kv_len rounded up to the page.  The host lengths
+// are accepted for API symmetry; the rule does not need them.
 int decode_attn_tuned_split_size(int64_t rows, int num_kv_heads, int max_kv_len,
                                  const int32_t *kv_lens_host)
 {
@@ -228,7 +278,7 @@ int decode_attn_tuned_split_size(int64_t rows, int num_kv_heads, int max_kv_len,
     (void)kv_lens_host;
     if (rows <= 0 || max_kv_len <= 0)
         return 16;
-    int S = rows <= 8 ? 1024 : 512;
+    int S = rows <= 4 ? 1024 : (rows <= 8 ? 512 : 256);
     const int cap = (max_kv_len + 15) / 16 * 16;
     while (S > 16 && S / 2 >= cap)
         S /= 2;

@@ -51,6 +51,20 @@ struct AttnArgs {
 };
 size_t attn_workspace_bytes(int64_t rows, int hq, int d, int max_kv_len, int split);
 hipError_t launch_decode_attn(const AttnArgs &a, hipStream_t s);
+struct PrefillArgs {
+    const uint16_t *q;
+    int64_t q_row_stride;
+    const uint16_t *k_cache, *v_cache;
+    const int32_t *block_table_row;
+    int64_t start, tokens;  // prompt positions start .. start + tokens - 1
+    uint16_t *out;
+    int64_t out_row_stride;
+    int hq, hkv, d, page, split;
+    float scale;
+    float *ws;  // split schedule only: [tokens, hq, nsplit_max] x (D + 2) floats
+};
+size_t prefill_workspace_bytes(int64_t tokens, int hq, int hkv, int d, int64_t start, int split);
+hipError_t launch_prefill_attn(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_kv_append(const uint16_t *k_new, int64_t ks, const uint16_t *v_new, int64_t vs,
                             const int32_t *slots, int64_t tokens, uint16_t *k_cache,
                             uint16_t *v_cache, int64_t num_pages, int hkv, int d, int page,

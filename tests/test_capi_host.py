@@ -126,9 +126,11 @@ def test_tuned_split_size_follows_the_batch():
     # 256 for every batch)
     one = rbi.decode_attn_tuned_split_size(1, 4, 32768, [32768])
     many = rbi.decode_attn_tuned_split_size(256, 4, 32768, [32768] * 256)
-    assert one == 1024 and many == 512
-    assert rbi.decode_attn_tuned_split_size(8, 4, 32768, None) == 1024
-    assert rbi.decode_attn_tuned_split_size(9, 4, 32768, None) == 512
+    assert one == 1024 and many == 256
+    assert rbi.decode_attn_tuned_split_size(4, 4, 32768, None) == 1024
+    assert rbi.decode_attn_tuned_split_size(5, 4, 32768, None) == 512
+    assert rbi.decode_attn_tuned_split_size(8, 4, 32768, None) == 512
+    assert rbi.decode_attn_tuned_split_size(9, 4, 32768, None) == 256
     # capped near short maximum lengths, always a multiple of the page
     short = rbi.decode_attn_tuned_split_size(1, 4, 100, None)
     assert short % 16 == 0 and 16 <= short <= 128
@@ -153,3 +155,42 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(2, 8, dtype=torch.bfloat16)
     with pytest.raises(rbi.RbiError):
         rbi.rmsnorm_bi(x, torch.ones(8, dtype=torch.bfloat16))
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, qs=64 * 128, kc=FAKE, vc=FAKE, bt=FAKE, start=0, tokens=700, out=FAKE,
+             os=64 * 128, hq=64, hkv=4, d=128, page=16, split=256, scale=0.088, ws=NULL, wsb=0)
+    a.update(kw)
+    return rbi.lib().prefill_attn_bi(a["q"], a["qs"], a["kc"], a["vc"], a["bt"], a["start"],
+                                     a["tokens"], a["out"], a["os"], a["hq"], a["hkv"], a["d"],
+                                     a["page"], a["split"], a["scale"], a["ws"], a["wsb"], NULL)
+
+
+def test_prefill_attn_validation():
+    assert _prefill(tokens=0) == OK
+    assert _prefill(tokens=-1) == EINVAL
+    assert _prefill(start=-1) == EINVAL
+    assert _prefill(d=96) == EUNSUPPORTED
+    assert _prefill(split=512) == EUNSUPPORTED     # more than one page pair per wave
+    assert _prefill(split=200) == EUNSUPPORTED     # not a multiple of the page
+    assert _prefill(page=32) == EUNSUPPORTED
+    assert _prefill(hq=64, hkv=2) == EUNSUPPORTED   # group of 32
+    assert _prefill(hq=63) == EINVAL
+    assert _prefill(q=NULL) == EINVAL
+    assert _prefill(bt=NULL) == EINVAL
+    assert _prefill(out=FAKE + 4) == EINVAL
+    assert _prefill(qs=64 * 128 - 8) == EINVAL
+    assert _prefill(start=1 << 30) == EUNSUPPORTED
+    # a short chunk after a long prefix runs the split schedule and needs a workspace
+    need = rbi.prefill_attn_workspace_size(40, 64, 4, 128, 1000, 256)
+    assert need == 40 * 64 * 5 * 130 * 4     # ceil(1040 / 256) = 5 splits
+    assert _prefill(tokens=40, start=1000) == EWORKSPACE
+    assert _prefill(tokens=40, start=1000, ws=FAKE, wsb=need - 1) == EWORKSPACE
+
+
+def test_prefill_workspace_follows_the_schedule():
+    # fused (no workspace) once ceil(tokens / 8) * num_kv_heads token blocks reach 256
+    assert rbi.prefill_attn_workspace_size(512, 64, 4, 128, 0, 256) == 0
+    assert rbi.prefill_attn_workspace_size(504, 64, 4, 128, 0, 256) > 0
+    assert rbi.prefill_attn_workspace_size(2048, 8, 1, 64, 100, 16) == 0
+    assert rbi.prefill_attn_workspace_size(0, 64, 4, 128, 0, 256) == 0

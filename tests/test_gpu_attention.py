@@ -1,5 +1,6 @@
 """GPU tests of decode_attn_bi / decode_attn_tuned / kv_append: parity with the
-CPU oracle (max|out - ref| <= 2e-2 * RMS(ref)) and bitwise invariance across
+CPU oracle (per row, max|out - ref| <= 2e-2 * RMS(ref) beyond the bf16 rounding of
+the output; see tests.conftest.attn_tol) and bitwise invariance across
 batch size, neighbours, order, page placement, grid extent (max_kv_len), KV
 growth across split boundaries and chunked versus unchunked prefill.
 """
@@ -12,6 +13,7 @@ import torch
 import invariant_rmsnorm_bi_amd as rbi
 import oracle
 import synth
+from tests.conftest import attn_tol
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -34,16 +36,7 @@ def _oracle(q, kv, scale, rows=None):
 
 
 def _tol_ok(out, ref):
-    """max|out - ref| <= 2e-2 * RMS(ref), per row: each row is its own attention
-    problem, and a batch-wide RMS would let the small outputs of long rows set the
-    bar for the larger outputs of short ones.  Returns (ok, worst ratio, its row)."""
-    o = out.double().cpu().numpy().reshape(ref.shape[0], -1)
-    r = ref.reshape(ref.shape[0], -1)
-    err = np.abs(o - r).max(1)
-    rms = np.sqrt(np.mean(r ** 2, 1))
-    ratio = err / rms
-    worst = int(np.argmax(ratio))
-    return bool((ratio <= 2e-2).all()), float(ratio[worst]), worst
+    return attn_tol(out, ref)
 
 
 def _run(fn, q, kv, max_len, **kw):

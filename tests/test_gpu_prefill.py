@@ -1,0 +1,130 @@
+"""GPU tests of prefill_attn_bi: every prompt token's output is bit-identical to
+the decode_attn_bi row with the same query, cache and length (so neither the
+chunking of a prompt nor a cached prefix can move its bits), within tolerance of
+the CPU oracle, and the same from run to run.  Both schedules are covered: the
+fused one (enough token blocks to fill the GPU, no workspace) and the split one
+(short chunks after a long prefix, partials staged in a workspace).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_rmsnorm_bi_amd as rbi
+import oracle
+import synth
+from tests.conftest import attn_tol
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+class Prompt:
+    """One request's prompt of `total` tokens: seeded K/V/q, pages placed by a seeded
+    permutation, caches NaN-filled where nothing was written."""
+
+    def __init__(self, total, hkv, hq, d, seed):
+        self.total, self.hkv, self.hq, self.d = total, hkv, hq, d
+        npages = -(-total // 16)
+        self.cache_pages = npages + 8
+        self.pages = synth.page_ids(self.cache_pages, seed=seed)[:npages].to(torch.int32).to(DEV)
+        self.k = synth.normal((total, hkv, d), seed=seed + 1).to(DEV)
+        self.v = synth.normal((total, hkv, d), seed=seed + 2).to(DEV)
+        self.q = synth.normal((total, hq, d), seed=seed + 3).to(DEV)
+        pos = torch.arange(total, device=DEV)
+        self.slots = (self.pages[pos // 16].long() * 16 + pos % 16).to(torch.int32)
+        self.kc = torch.full((self.cache_pages, hkv, 16, d), float("nan"), dtype=torch.bfloat16,
+                             device=DEV)
+        self.vc = torch.full((self.cache_pages, hkv, d, 16), float("nan"), dtype=torch.bfloat16,
+                             device=DEV)
+
+    def append(self, a, b):
+        rbi.kv_append(self.k[a:b], self.v[a:b], self.slots[a:b].contiguous(), self.kc, self.vc)
+
+    def prefill(self, a, b, split):
+        return rbi.prefill_attn_bi(self.q[a:b].contiguous(), self.kc, self.vc, self.pages, a,
+                                   split, scale=1 / math.sqrt(self.d))
+
+    def decode_rows(self, a, b, split):
+        n = b - a
+        bt = self.pages[None].repeat(n, 1).contiguous()
+        lens = torch.arange(a + 1, b + 1, dtype=torch.int32, device=DEV)
+        return rbi.decode_attn_bi(self.q[a:b].contiguous(), self.kc, self.vc, bt, lens, b, split,
+                                  scale=1 / math.sqrt(self.d))
+
+    def oracle_rows(self, rows):
+        rows = np.asarray(rows)
+        bt = np.repeat(self.pages.cpu().numpy()[None], len(rows), 0)
+        return oracle.decode_attn(synth.bf16_bits(self.q.cpu()[rows]),
+                                  synth.bf16_bits(self.kc.cpu()), synth.bf16_bits(self.vc.cpu()),
+                                  bt, (rows + 1).astype(np.int32), 1 / math.sqrt(self.d))
+
+
+CASES = [
+    # d, hq, hkv, split, start, tokens      schedule
+    (128, 64, 4, 256, 0, 700),            # fused, every length from 1 to 700
+    (128, 64, 4, 256, 1000, 40),          # split: a short chunk after a long prefix
+    (64, 8, 1, 16, 0, 100),               # split, one-page splits, group of 8
+    (128, 16, 2, 64, 37, 333),            # split, ragged start and count
+    (64, 32, 4, 128, 5, 2049),            # fused, head_dim 64, ragged last block
+    (128, 4, 4, 256, 0, 1),               # one token, group of one
+    (128, 64, 8, 256, 3000, 513),         # fused, group of 8, long prefix
+    (128, 64, 4, 32, 250, 2100),          # fused, many splits per token
+]
+
+
+@pytest.mark.parametrize("d,hq,hkv,split,start,tokens", CASES)
+def test_prefill_equals_decode_rows(d, hq, hkv, split, start, tokens):
+    print(f"prefill case d={d} hq={hq} hkv={hkv} split={split} start={start} tokens={tokens}",
+          flush=True)
+    p = Prompt(start + tokens, hkv, hq, d, seed=31)
+    p.append(0, start + tokens)
+    out = p.prefill(start, start + tokens, split)
+    ref_rows = p.decode_rows(start, start + tokens, split)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any()
+    diff = (out != ref_rows).reshape(tokens, -1).any(1).nonzero().flatten().tolist()
+    assert not diff, f"tokens differing from their decode rows: {diff[:10]}"
+    # the oracle on sampled tokens (first, last, split edges, seeded others)
+    rng = np.random.default_rng(tokens)
+    pick = {0, tokens - 1} | set(rng.integers(0, tokens, size=6).tolist())
+    pick |= {t for t in range(tokens) if (start + t + 1) % split in (0, 1)}
+    rows = sorted(pick)[:24]
+    ok, ratio, worst = attn_tol(out[rows], p.oracle_rows([start + t for t in rows]))
+    assert ok, (ratio, rows[worst])
+
+
+def test_prefill_schedules_as_documented():
+    # the fused schedule (no workspace) once token blocks fill the GPU
+    assert rbi.prefill_attn_workspace_size(700, 64, 4, 128, 0, 256) == 0
+    assert rbi.prefill_attn_workspace_size(40, 64, 4, 128, 1000, 256) > 0
+
+
+def test_chunked_prefill_is_bitwise_unchunked():
+    # one 1500-token prompt: a single call (fused) versus seeded random chunks (fused
+    # and split schedules), each chunk appended just before it attends, so cache
+    # slots past the chunk still hold NaN while it runs
+    T, HKV, HQ, D, S = 1500, 4, 64, 128, 256
+    full_p = Prompt(T, HKV, HQ, D, seed=41)
+    full_p.append(0, T)
+    full = full_p.prefill(0, T, S)
+    chunk_p = Prompt(T, HKV, HQ, D, seed=41)
+    rng = np.random.default_rng(42)
+    cuts = sorted(set(rng.integers(1, T, size=7).tolist()) | {1, 1100})
+    bounds = [0] + cuts + [T]
+    chunked = torch.empty_like(full)
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        chunk_p.append(a, b)
+        chunked[a:b] = chunk_p.prefill(a, b, S)
+    torch.cuda.synchronize()
+    assert torch.equal(full, chunked), bounds
+    assert not torch.isnan(full.float()).any()
+
+
+def test_prefill_run_to_run():
+    p = Prompt(900, 4, 64, 128, seed=51)
+    p.append(0, 900)
+    first = p.prefill(100, 900, 256)
+    for _ in range(5):
+        assert torch.equal(p.prefill(100, 900, 256), first)
