@@ -309,6 +309,30 @@ def prefill_points():
     return pts
 
 
+def sampling_points():
+    """sample_gumbel over the decode layer's lm_head logits (fp32 [rows, 151936],
+    N(0, 2) values, per-row seeds and positions, temperature 0.8) at 1 and 128
+    rows, against the greedy rbi_argmax_rows over the same logits: device time
+    (median of 20) and the logits' read rate."""
+    pts = []
+    V = 151936
+    for rows in (1, 128):
+        x = synth.normal((rows, V), std=2.0, seed=74, dtype=torch.float32, device=DEV)
+        seeds = torch.arange(rows, dtype=torch.int64, device=DEV) * 7919 + 5
+        pos = torch.arange(rows, dtype=torch.int64, device=DEV) + 1000
+        temps = torch.full((rows,), 0.8, device=DEV)
+        ws = torch.empty(rbi.sample_gumbel_workspace_size(rows, V), dtype=torch.uint8, device=DEV)
+        tok = torch.empty(rows, dtype=torch.int32, device=DEV)
+        t_s = time_fn(lambda: rbi.sample_gumbel(x, seeds, pos, temps, out=tok, workspace=ws))
+        t_g = time_fn(lambda: rbi.argmax_rows(x))
+        nbytes = rows * V * 4
+        pts.append({"point": f"sample_gumbel rows={rows} vocab={V}", "us": round(t_s * 1e3, 2),
+                    "GB/s": round(nbytes / (t_s * 1e-3) / 1e9, 1),
+                    "greedy_argmax_us": round(t_g * 1e3, 2)})
+        del x, ws
+    return pts
+
+
 # --------------------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample of the same workload)
 # --------------------------------------------------------------------------------------
@@ -433,7 +457,7 @@ def main():
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the end-to-end decode-layer comparison")
     ap.add_argument("--no-prefill", action="store_true",
-                    help="skip the prefill-attention comparison")
+                    help="skip the prefill-attention and sampling legs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB copy (counter calibration for profiles/)")
     args = ap.parse_args()
@@ -515,6 +539,11 @@ def main():
         prefill = {"points": prefill_points(),
                    "unit": "device us; TFLOP/s of the algorithmic 4*Hq*D*sum(L) MFMA work"}
 
+    sampling = None
+    if not args.no_prefill:
+        log("timing seeded sampling")
+        sampling = {"points": sampling_points()}
+
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample")
@@ -531,7 +560,7 @@ def main():
                                 "(64q/4kv heads, d128, page 16, split 256, L~U{1..32768})"),
                    "step_bytes": step_bytes, "buffer_sets": SETS},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "twins": twins,
-        "prefill": prefill,
+        "prefill": prefill, "sampling": sampling,
         "fingerprint": fingerprint(),
     }
     print(json.dumps(rec), flush=True)

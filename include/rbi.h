@@ -248,6 +248,37 @@ int prefill_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, co
                     size_t workspace_bytes, void *stream);
 
 /*
+ * sample_gumbel: seeded Gumbel-max sampling, one token per row ([P1] section 9.3
+ * "Non-Greedy Sampling Can Be Deterministic Too").  A counter-based hash of
+ * (seed, position, vocabulary id) supplies Gumbel noise that is added to the
+ * scaled logits, so a sample is a pure function of the logits and the seed at
+ * any temperature.  For row r with T = temperatures[r] > 0:
+ *     tokens[r] = argmax_i (logits[r,i] / T + g_i),   g_i = -ln(-ln u_i),
+ * u_i = (floor(w / 2^9) + 1/2) / 2^23, w = word (i mod 4) of Philox4x32-10
+ * (Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) with
+ * counter (i / 4, positions[r] mod 2^32, positions[r] / 2^32, 0) and key
+ * (seeds[r] mod 2^32, seeds[r] / 2^32).  T <= 0 is greedy (argmax of the
+ * logits).  NaN logits are never chosen; among equal scores the lowest index
+ * wins; a row of NaNs gives 0.  The noise depends only on (seed, position,
+ * vocabulary id) and the argmax is exact, so a row's token depends on nothing
+ * but its own logits and parameters: batch-invariant whenever the logits are.
+ * To vary samples across requests, give each request its own seed.
+ *  logits        [rows, vocab] fp32, row stride logits_row_stride (a multiple of
+ *                4, >= vocab), 16-byte aligned
+ *  seeds         [rows] uint64 (device)
+ *  positions     [rows] int64 (device), the token position being sampled
+ *  temperatures  [rows] fp32 (device)
+ *  tokens        [rows] int32 (device), written
+ *  workspace     >= sample_gumbel_workspace_size(rows, vocab) bytes, 16-byte
+ *                aligned: per-chunk partials
+ * Limits: vocab < 2^31 - 16, rows <= 65535.  rows == 0 is a no-op.
+ */
+size_t sample_gumbel_workspace_size(int64_t rows, int64_t vocab);
+int sample_gumbel(const float *logits, int64_t logits_row_stride, int64_t rows, int64_t vocab,
+                  const uint64_t *seeds, const int64_t *positions, const float *temperatures,
+                  int32_t *tokens, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * kv_append: write new tokens' K and V into their cache slots BEFORE attention
  * runs, so cached and fresh tokens are reduced as one sequence with the same
  * split boundaries ([P1] section 5.5: update the KV cache and page table before

@@ -12,6 +12,7 @@ Entry points (see include/rbi.h for the exact contracts):
   matmul_bi / matmul_tuned
   decode_attn_bi / decode_attn_tuned
   prefill_attn_bi
+  sample_gumbel
   kv_append, embed, residual_add, swiglu, argmax_rows
 """
 from __future__ import annotations
@@ -26,7 +27,8 @@ __all__ = [
     "RbiError", "lib", "lib_path", "rmsnorm_bi", "rmsnorm_tuned", "matmul_bi", "matmul_tuned",
     "matmul_tuned_workspace_size", "decode_attn_bi", "decode_attn_tuned",
     "decode_attn_workspace_size", "decode_attn_tuned_split_size", "prefill_attn_bi",
-    "prefill_attn_workspace_size", "kv_append", "embed",
+    "prefill_attn_workspace_size", "sample_gumbel", "sample_gumbel_workspace_size",
+    "kv_append", "embed",
     "residual_add", "swiglu", "argmax_rows", "EXPORTS",
 ]
 
@@ -40,7 +42,8 @@ EXPORTS = (
     "rbi_status_string", "rbi_abi_version", "rmsnorm_bi", "rmsnorm_tuned", "matmul_bi",
     "matmul_tuned", "matmul_tuned_workspace_size", "decode_attn_workspace_size",
     "decode_attn_bi", "decode_attn_tuned_split_size", "decode_attn_tuned",
-    "prefill_attn_workspace_size", "prefill_attn_bi", "kv_append",
+    "prefill_attn_workspace_size", "prefill_attn_bi", "sample_gumbel_workspace_size",
+    "sample_gumbel", "kv_append",
     "rbi_embed", "rbi_residual_add", "rbi_swiglu", "rbi_argmax_rows",
 )
 
@@ -85,6 +88,8 @@ def lib() -> ctypes.CDLL:
         "prefill_attn_workspace_size": ([i64, i32, i32, i32, i64, i32], sz),
         "prefill_attn_bi": ([p, i64, p, p, p, i64, i64, p, i64, i32, i32, i32, i32, i32, f32, p,
                              sz, p], i32),
+        "sample_gumbel_workspace_size": ([i64, i64], sz),
+        "sample_gumbel": ([p, i64, i64, i64, p, p, p, p, p, sz, p], i32),
         "kv_append": ([p, i64, p, i64, p, i64, p, p, i64, i32, i32, i32, p], i32),
         "rbi_embed": ([p, i64, i64, p, i64, p, i64, p], i32),
         "rbi_residual_add": ([p, p, p, i64, p], i32),
@@ -346,6 +351,43 @@ def prefill_attn_bi(q, k_cache, v_cache, block_table_row, start_pos: int,
                                _lead_stride(out), hq, hkv, d, page, split_size, float(scale),
                                _ptr(workspace), ws_bytes, _stream())
     _check(st, "prefill_attn_bi")
+    return out
+
+
+def sample_gumbel_workspace_size(rows: int, vocab: int) -> int:
+    return int(lib().sample_gumbel_workspace_size(rows, vocab))
+
+
+def sample_gumbel(logits: torch.Tensor, seeds, positions, temperatures, out=None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Seeded Gumbel-max sampling of fp32 logits [rows, vocab]: per row,
+    argmax(logit / T + Gumbel noise of (seed, position, vocab id)); greedy when
+    T <= 0.  seeds (uint64 values), positions and temperatures are per-row device
+    tensors or sequences.  Returns int32 tokens [rows]."""
+    _need_cuda(logits)
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1:
+        raise RbiError("logits must be fp32 [rows, vocab] with unit inner stride")
+    rows, vocab = logits.shape
+    dev = logits.device
+
+    def dev_tensor(v, dtype):
+        t = v if isinstance(v, torch.Tensor) else torch.as_tensor(v)
+        return t.to(device=dev, dtype=dtype).contiguous().reshape(rows)
+
+    s = seeds if isinstance(seeds, torch.Tensor) else torch.as_tensor(
+        [int(x) - (1 << 64) if int(x) >= (1 << 63) else int(x) for x in seeds], dtype=torch.int64)
+    s = dev_tensor(s, torch.int64)          # uint64 bits carried in int64
+    p = dev_tensor(positions, torch.int64)
+    t = dev_tensor(temperatures, torch.float32)
+    if out is None:
+        out = torch.empty(rows, dtype=torch.int32, device=dev)
+    need = sample_gumbel_workspace_size(rows, vocab)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = lib().sample_gumbel(_ptr(logits), _lead_stride(logits), rows, vocab, _ptr(s), _ptr(p),
+                             _ptr(t), _ptr(out), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream())
+    _check(st, "sample_gumbel")
     return out
 
 

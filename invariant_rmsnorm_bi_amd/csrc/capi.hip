@@ -264,6 +264,33 @@ int prefill_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, co
     return launched(rbi::launch_prefill_attn(a, stream_of(stream)));
 }
 
+size_t sample_gumbel_workspace_size(int64_t rows, int64_t vocab)
+{
+    if (rows <= 0 || vocab <= 0)
+        return 0;
+    return rbi::sample_workspace_bytes(rows, vocab);
+}
+
+int sample_gumbel(const float *logits, int64_t logits_row_stride, int64_t rows, int64_t vocab,
+                  const uint64_t *seeds, const int64_t *positions, const float *temperatures,
+                  int32_t *tokens, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (rows < 0 || vocab < 1 || logits_row_stride < vocab || logits_row_stride % 4)
+        return RBI_EINVAL;
+    if (rows == 0)
+        return RBI_OK;
+    if (!logits || !seeds || !positions || !temperatures || !tokens || !aligned16(logits))
+        return RBI_EINVAL;
+    if (vocab > (int64_t)0x7ffffff0 || rows > kGridYZ)
+        return RBI_EUNSUPPORTED;
+    const size_t need = rbi::sample_workspace_bytes(rows, vocab);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return RBI_EWORKSPACE;
+    return launched(rbi::launch_sample_gumbel(logits, logits_row_stride, rows, vocab, seeds,
+                                              positions, temperatures, tokens, workspace,
+                                              stream_of(stream)));
+}
+
 // Split size of the twin, tuned to the batch: the fastest split size measured on
 // MI355X for the kernels here (decode batches of 64 query / 4 kv heads, d128,
 // lengths up to 32768): 1024 tokens for at most 4 rows, 512 for at most 8 (few

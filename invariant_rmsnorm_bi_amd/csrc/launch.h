@@ -70,6 +70,13 @@ hipError_t launch_kv_append(const uint16_t *k_new, int64_t ks, const uint16_t *v
                             uint16_t *v_cache, int64_t num_pages, int hkv, int d, int page,
                             hipStream_t s);
 
+// sampling.hip
+int sample_chunks(int64_t vocab);
+size_t sample_workspace_bytes(int64_t rows, int64_t vocab);
+hipError_t launch_sample_gumbel(const float *logits, int64_t ld, int64_t rows, int64_t vocab,
+                                const uint64_t *seeds, const int64_t *positions,
+                                const float *temps, int32_t *tokens, void *ws, hipStream_t s);
+
 // glue.hip
 hipError_t launch_embed(const uint16_t *table, int64_t vocab, int64_t hidden, const int32_t *ids,
                         int64_t rows, uint16_t *out, int64_t os, hipStream_t s);

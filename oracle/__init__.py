@@ -60,6 +60,9 @@ def lib():
         L.orc_decode_attn_split.argtypes = [p, i64, p, p, p, i64, p, p, i64, i32, i32, i32, i32,
                                              d, i64]
         L.orc_split_plan.argtypes = [i64, i64, p, i64]
+        L.orc_philox4x32_10.argtypes = [p, p, p]
+        L.orc_gumbel_noise.argtypes = [ctypes.c_uint64, i64, i64, p]
+        L.orc_sample_gumbel.argtypes = [p, i64, i64, i64, p, p, p, p, p, p]
         L.orc_split_plan.restype = i64
         _lib = L
     return _lib
@@ -192,3 +195,38 @@ def argmax_lowest(x: np.ndarray) -> np.ndarray:
     x = np.asarray(x)
     assert not np.isnan(x).any()
     return np.argmax(x, axis=-1)  # numpy returns the first occurrence of the maximum
+
+
+def philox4x32_10(ctr, key) -> tuple:
+    """Philox4x32-10 (Salmon et al., SC 2011) of a 4-word counter and a 2-word key."""
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint32))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32))
+    out = np.zeros(4, dtype=np.uint32)
+    lib().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return tuple(int(x) for x in out)
+
+
+def gumbel_noise(seed: int, position: int, n: int) -> np.ndarray:
+    """Gumbel noise g_0 .. g_{n-1} of one (seed, position): -ln(-ln u) with u from
+    Philox4x32-10 (see orc_gumbel_noise), float64."""
+    g = np.zeros(n, dtype=np.float64)
+    lib().orc_gumbel_noise(int(seed) & (2**64 - 1), int(position), int(n), _ptr(g))
+    return g
+
+
+def sample_gumbel(logits: np.ndarray, seeds, positions, temperatures):
+    """Seeded Gumbel-max sampling per row (hidekazu-konishi.com, section 9.3):
+    token = argmax(logit / T + g), greedy when T <= 0.  logits: fp32 [rows, vocab].
+    Returns (tokens int32 [rows], best score float64 [rows], gap to the runner-up
+    float64 [rows])."""
+    x = np.ascontiguousarray(logits, dtype=np.float32)
+    rows, vocab = x.shape
+    sd = np.ascontiguousarray(np.asarray(seeds, dtype=np.uint64).reshape(rows))
+    ps = np.ascontiguousarray(np.asarray(positions, dtype=np.int64).reshape(rows))
+    tp = np.ascontiguousarray(np.asarray(temperatures, dtype=np.float32).reshape(rows))
+    tok = np.zeros(rows, dtype=np.int32)
+    best = np.zeros(rows, dtype=np.float64)
+    gap = np.zeros(rows, dtype=np.float64)
+    lib().orc_sample_gumbel(_ptr(x), vocab, rows, vocab, _ptr(sd), _ptr(ps), _ptr(tp), _ptr(tok),
+                            _ptr(best), _ptr(gap))
+    return tok, best, gap

@@ -295,3 +295,108 @@ void orc_decode_attn_split(const uint16_t *q, int64_t q_row_stride,
         }
     }
 }
+
+/*
+ * Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3" (SC 2011), written here from
+ * that definition: a 128-bit counter (c0, c1, c2, c3) and a 64-bit key (k0, k1)
+ * go through ten rounds; each round multiplies c0 and c2 by the two round
+ * multipliers as 32x32 -> 64-bit products, and the new counter is
+ *     (hi(M1*c2) ^ c1 ^ k0, lo(M1*c2), hi(M0*c0) ^ c3 ^ k1, lo(M0*c0));
+ * between rounds the key advances by the two Weyl constants (golden ratio and
+ * sqrt(3) - 1 in 32-bit fixed point).  The result is the final counter.
+ */
+void orc_philox4x32_10(const uint32_t *ctr, const uint32_t *key, uint32_t *out)
+{
+    const uint64_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    uint32_t c[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        const uint64_t p0 = M0 * (uint64_t)c[0];
+        const uint64_t p1 = M1 * (uint64_t)c[2];
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+        const uint32_t n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+        const uint32_t n3 = (uint32_t)p0;
+        c[0] = n0;
+        c[1] = n1;
+        c[2] = n2;
+        c[3] = n3;
+    }
+    memcpy(out, c, sizeof c);
+}
+
+/*
+ * Gumbel noise of vocabulary entries 0 .. n-1 for one (seed, position) pair
+ * (seeded Gumbel-max sampling: [P1] section 9.3 "Non-Greedy Sampling Can Be
+ * Deterministic Too" -- noise from a counter-based hash instead of a stateful
+ * generator makes a sample a pure function of the logits and the seed).  Entry
+ * i takes word
+ * i mod 4 of Philox4x32-10 with counter (i / 4, position low 32 bits, position
+ * high 32 bits, 0) and key (seed low 32 bits, seed high 32 bits); the word's top
+ * 23 bits give u = (floor(w / 2^9) + 1/2) / 2^23 in (0, 1), and the noise is
+ * the standard Gumbel quantile g = -ln(-ln u).
+ */
+static double gumbel_of_word(uint32_t w)
+{
+    const double u = ((double)(w >> 9) + 0.5) / 8388608.0;
+    return -log(-log(u));
+}
+
+void orc_gumbel_noise(uint64_t seed, int64_t position, int64_t n, double *g)
+{
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    for (int64_t i = 0; i < n; ++i) {
+        const uint32_t ctr[4] = {(uint32_t)(i / 4), (uint32_t)(uint64_t)position,
+                                 (uint32_t)((uint64_t)position >> 32), 0u};
+        uint32_t w[4];
+        orc_philox4x32_10(ctr, key, w);
+        g[i] = gumbel_of_word(w[i % 4]);
+    }
+}
+
+/*
+ * Seeded Gumbel-max sampling of each row: token = argmax_i (logit_i / T + g_i),
+ * g from orc_gumbel_noise(seed_r, position_r); T <= 0 means greedy (argmax of
+ * the logits).  NaN logits are never chosen; among equal scores the lowest index
+ * wins; a row of NaNs gives token 0.  Also returns the best score and the gap to
+ * the runner-up (infinite when there is none), from which a test can tell a
+ * clear decision from a near tie.
+ */
+void orc_sample_gumbel(const float *logits, int64_t ld, int64_t rows, int64_t vocab,
+                       const uint64_t *seeds, const int64_t *positions, const float *temps,
+                       int32_t *tokens, double *best, double *gap)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double T = (double)temps[r];
+        double *g = (double *)malloc((size_t)(vocab > 0 ? vocab : 1) * sizeof(double));
+        if (T > 0.0)
+            orc_gumbel_noise(seeds[r], positions[r], vocab, g);
+        double b1 = -INFINITY, b2 = -INFINITY;
+        int64_t i1 = -1;
+        for (int64_t i = 0; i < vocab; ++i) {
+            const double x = (double)logits[r * ld + i];
+            if (isnan(x))
+                continue;
+            const double s = T > 0.0 ? x / T + g[i] : x;
+            if (i1 < 0 || s > b1) {
+                if (i1 >= 0)
+                    b2 = b1;
+                b1 = s;
+                i1 = i;
+            } else if (s > b2) {
+                b2 = s;
+            }
+        }
+        tokens[r] = i1 < 0 ? 0 : (int32_t)i1;
+        best[r] = b1;
+        gap[r] = b1 - b2;
+        free(g);
+    }
+}

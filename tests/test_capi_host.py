@@ -194,3 +194,19 @@ def test_prefill_workspace_follows_the_schedule():
     assert rbi.prefill_attn_workspace_size(504, 64, 4, 128, 0, 256) > 0
     assert rbi.prefill_attn_workspace_size(2048, 8, 1, 64, 100, 16) == 0
     assert rbi.prefill_attn_workspace_size(0, 64, 4, 128, 0, 256) == 0
+
+
+def test_sample_gumbel_validation():
+    f = rbi.lib().sample_gumbel
+    need = rbi.sample_gumbel_workspace_size(4, 151936)
+    assert need == 4 * 38 * 8                      # ceil(151936 / 4096) chunks of (score, index)
+    assert f(FAKE, 151936, 0, 151936, FAKE, FAKE, FAKE, FAKE, FAKE, need, NULL) == OK
+    assert f(FAKE, 151934, 4, 151936, FAKE, FAKE, FAKE, FAKE, FAKE, need, NULL) == EINVAL  # ld < vocab
+    assert f(FAKE, 151938, 4, 151936, FAKE, FAKE, FAKE, FAKE, FAKE, need, NULL) == EINVAL  # ld % 4
+    assert f(FAKE + 4, 151936, 4, 151936, FAKE, FAKE, FAKE, FAKE, FAKE, need, NULL) == EINVAL
+    assert f(FAKE, 151936, 4, 151936, NULL, FAKE, FAKE, FAKE, FAKE, need, NULL) == EINVAL
+    assert f(FAKE, 151936, 4, 151936, FAKE, FAKE, FAKE, NULL, FAKE, need, NULL) == EINVAL
+    assert f(FAKE, 151936, 4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, need, NULL) == EINVAL
+    assert f(FAKE, 151936, -1, 151936, FAKE, FAKE, FAKE, FAKE, FAKE, need, NULL) == EINVAL
+    assert f(FAKE, 151936, 4, 151936, FAKE, FAKE, FAKE, FAKE, NULL, need, NULL) == EWORKSPACE
+    assert f(FAKE, 151936, 4, 151936, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, NULL) == EWORKSPACE

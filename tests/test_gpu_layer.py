@@ -208,3 +208,70 @@ def test_graph_replay_equals_eager_steps(weights):
         assert torch.equal(tk_e, tk_g), i
         tok = tk_e.cpu().numpy()
 
+
+
+def test_seeded_sampling_reproducible_in_any_batch(weights):
+    # non-greedy decoding (temperature 0.8, the probe's own seed) on top of the
+    # invariant layer: the probe's sampled tokens are the same alone and inside
+    # random continuous batches; another seed samples another sequence
+    import invariant_rmsnorm_bi_amd as rbi
+    rng = np.random.default_rng(77)
+    prompt = rng.integers(0, CFG.vocab, 40).tolist()
+    steps, seed, T = 24, 2**63 + 12345, 0.8
+    pages = (40 + steps + 15) // 16
+
+    def sample(lg, pos_list, seed_list):
+        return rbi.sample_gumbel(lg, seed_list, pos_list, [T] * len(pos_list)).cpu().tolist()
+
+    def run_alone(sd):
+        layer = DecodeLayer(CFG, weights, num_pages=pages + 1)
+        table = _table(np.arange(pages))
+        lg, _ = layer.step(prompt, np.stack([table] * 40), list(range(40)))
+        tok = sample(lg[-1:], [40], [sd])[0]
+        out = [tok]
+        for i in range(steps - 1):
+            lg, _ = layer.step([tok], table[None], [40 + i])
+            tok = sample(lg, [41 + i], [sd])[0]
+            out.append(tok)
+        return out
+
+    ref = run_alone(seed)
+    assert run_alone(seed + 1) != ref
+
+    n_fill = 31
+    fill_lens = synth.uniform_lengths(n_fill, 1, 8000, seed=78)
+    need = [(L + steps + 15) // 16 for L in fill_lens]
+    total = sum(need) + pages + 1
+    perm = synth.page_ids(total, seed=79).numpy()
+    layer = DecodeLayer(CFG, weights, num_pages=total)
+    layer.k_cache.copy_(synth.normal(layer.k_cache.shape, seed=80, device=DEV))
+    layer.v_cache.copy_(synth.normal(layer.v_cache.shape, seed=81, device=DEV))
+    tables, off = [], 0
+    for n in need:
+        tables.append(_table(perm[off:off + n]))
+        off += n
+    probe_table = _table(perm[off:off + pages])
+    pos = list(fill_lens)
+    tok = rng.integers(0, CFG.vocab, n_fill).tolist()
+    fseeds = rng.integers(0, 2**62, n_fill).tolist()
+    lg, _ = layer.step(prompt, np.stack([probe_table] * 40), list(range(40)))
+    p_tok = sample(lg[-1:], [40], [seed])[0]
+    got = [p_tok]
+    for step in range(steps - 1):
+        B = int(rng.integers(1, 33))
+        others = rng.choice(n_fill, size=B - 1, replace=False).tolist()
+        at = int(rng.integers(0, B))
+        members = others[:at] + [-1] + others[at:]
+        rows_tok = [p_tok if m < 0 else tok[m] for m in members]
+        rows_tab = [probe_table if m < 0 else tables[m] for m in members]
+        rows_pos = [40 + step if m < 0 else pos[m] for m in members]
+        lg, _ = layer.step(rows_tok, np.stack(rows_tab), rows_pos)
+        nxt = sample(lg, [p + 1 for p in rows_pos],
+                     [seed if m < 0 else fseeds[m] for m in members])
+        for i, m in enumerate(members):
+            if m >= 0:
+                tok[m] = nxt[i]
+                pos[m] += 1
+        p_tok = nxt[at]
+        got.append(p_tok)
+    assert got == ref
