@@ -40,6 +40,11 @@ namespace {
 
 constexpr int PAGE = 16;
 constexpr int WAVES = 8;   // waves per split workgroup
+// Row padding of the LDS stash of the waves' accumulators, in floats: a wave
+// writes head 4 * lane_group + j at d = 16 * db + lane % 16, so with rows of
+// D + 4 floats the four lane groups start 16 banks apart and a write is free
+// of bank conflicts (with unpadded rows all four hit the same banks).
+constexpr int CPAD = 4;
 
 template <int D>
 struct AttnK {
@@ -243,7 +248,7 @@ template <int D>
 __device__ __forceinline__ void stash_wave(float m_run, float l_run,
                                            const f32x4_t (&acc)[AttnK<D>::DB], int wave,
                                            const PairLanes &ln, float (*c_m)[16],
-                                           float (*c_l)[16], float (*c_acc)[16][D])
+                                           float (*c_l)[16], float (*c_acc)[16][D + CPAD])
 {
     float l_w = l_run;
     l_w += __shfl_xor(l_w, 16, kWave);
@@ -284,7 +289,8 @@ __device__ __forceinline__ void combine_ml(const float (*c_m)[16], const float (
 }
 
 template <int D, int EPT>
-__device__ __forceinline__ void combine_acc(const float (*c_acc)[16][D], const float (&cw)[WAVES],
+__device__ __forceinline__ void combine_acc(const float (*c_acc)[16][D + CPAD],
+                                            const float (&cw)[WAVES],
                                             int h, int dq, float (&o)[EPT])
 {
 #pragma unroll
@@ -318,7 +324,7 @@ __global__ __launch_bounds__(512, 4) void attn_split_kernel(
     using P = AttnK<D>;
     __shared__ __attribute__((aligned(16))) uint16_t q_lds[16][D];
     __shared__ float c_m[WAVES][16], c_l[WAVES][16];
-    __shared__ __attribute__((aligned(16))) float c_acc[WAVES][16][D];
+    __shared__ __attribute__((aligned(16))) float c_acc[WAVES][16][D + CPAD];
 
     const int s = blockIdx.x, g = blockIdx.y;
     const int64_t r = blockIdx.z;
@@ -517,9 +523,12 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
     using P = AttnK<D>;
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
     constexpr int EPT = D / 32;
+    // the stash is double-buffered: token n stashes into buffer n % 2 while the
+    // other buffer may still be read by the previous token's combine, so one
+    // barrier per token suffices
     __shared__ __attribute__((aligned(16))) uint16_t q_lds[TG][16][D];
-    __shared__ float c_m[WAVES][16], c_l[WAVES][16];
-    __shared__ __attribute__((aligned(16))) float c_acc[WAVES][16][D];
+    __shared__ float c_m[2][WAVES][16], c_l[2][WAVES][16];
+    __shared__ __attribute__((aligned(16))) float c_acc[2][WAVES][16][D + CPAD];
 
     const int nblk = FUSED ? gridDim.x : gridDim.z;
     // the blocks with the longest lengths (the most splits) are dispatched first
@@ -559,6 +568,8 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
             ot[t][e] = 0.f;
     }
 
+    __syncthreads();  // q_lds staged
+    int buf = 0;
     for (int s = s_first; s < s_end; ++s) {
         const int t0 = s * S;
         const int vp_blk = (min(t0 + S, Lmax) - t0 + PAGE - 1) / PAGE;
@@ -566,7 +577,6 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
         PairFrag<D> f;
         if (wave < (vp_blk + 1) / 2)
             load_pair<D>(f, wave, my_page, vp_blk, k_cache, v_cache, hkv, g, ln);
-        __syncthreads();  // q_lds staged (first split); the previous split's combine done
 #pragma unroll
         for (int t = 0; t < TG; ++t) {
             const int Lt = start + tok0 + t + 1;
@@ -591,13 +601,13 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
                                          m_run, l_run, acc);
                 }
             }
-            stash_wave<D>(m_run, l_run, acc, wave, ln, c_m, c_l, c_acc);
-            __syncthreads();
+            stash_wave<D>(m_run, l_run, acc, wave, ln, c_m[buf], c_l[buf], c_acc[buf]);
+            __syncthreads();  // this token's stash complete; every combine before the last done
             float Ms, ls, cw[WAVES];
-            combine_ml<D>(c_m, c_l, h, Ms, ls, cw);
+            combine_ml<D>(c_m[buf], c_l[buf], h, Ms, ls, cw);
             if (h < G) {
                 float os[EPT];
-                combine_acc<D, EPT>(c_acc, cw, h, dq, os);
+                combine_acc<D, EPT>(c_acc[buf], cw, h, dq, os);
                 if constexpr (FUSED) {
                     const float Mn = fmaxf(Mt[t], Ms);
                     const float al = exp2_hw(Mt[t] - Mn), be = exp2_hw(Ms - Mn);
@@ -619,7 +629,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
                     }
                 }
             }
-            __syncthreads();  // the stash is reused by the next token
+            buf ^= 1;
         }
     }
 
@@ -696,25 +706,30 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-constexpr int kPrefillTG = 8;  // prompt tokens per prefill workgroup
+// Prompt tokens per prefill workgroup: as many as fit in LDS beside the
+// double-buffered stash (at head_dim 128: 6 x 4 KiB of queries + 2 x 66 KiB).
+constexpr int prefill_tg(int d)
+{
+    return d == 128 ? 6 : 8;
+}
 
 // The fused prefill schedule needs enough token blocks to occupy the chip (one
 // workgroup per compute unit); short chunks use the split schedule.
-bool prefill_fused(int64_t tokens, int hkv)
+bool prefill_fused(int64_t tokens, int hkv, int d)
 {
-    const int64_t blocks = (tokens + kPrefillTG - 1) / kPrefillTG;
+    const int64_t blocks = (tokens + prefill_tg(d) - 1) / prefill_tg(d);
     return blocks * hkv >= 256;
 }
 
 template <int D>
 hipError_t launch_prefill_d(const PrefillArgs &a, hipStream_t s)
 {
-    constexpr int TG = kPrefillTG;
+    constexpr int TG = prefill_tg(D);
     const int nblk = (int)((a.tokens + TG - 1) / TG);
     const int nsmax = (int)((a.start + a.tokens + a.split - 1) / a.split);
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const dim3 blk(WAVES * 64);
-    if (prefill_fused(a.tokens, a.hkv)) {
+    if (prefill_fused(a.tokens, a.hkv, D)) {
         attn_prefill_kernel<D, TG, true><<<dim3((unsigned)nblk, (unsigned)a.hkv), blk, 0, s>>>(
             a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table_row, (int)a.start,
             (int)a.tokens, a.hq, a.hkv, a.split, scale_log2, a.out, a.out_row_stride, nsmax,
@@ -753,7 +768,7 @@ hipError_t launch_decode_attn(const AttnArgs &a, hipStream_t s)
 
 size_t prefill_workspace_bytes(int64_t tokens, int hq, int hkv, int d, int64_t start, int split)
 {
-    if (prefill_fused(tokens, hkv))
+    if (prefill_fused(tokens, hkv, d))
         return 0;
     const int64_t nsmax = (start + tokens + split - 1) / split;
     return (size_t)(tokens * hq * nsmax) * (size_t)(d + 2) * sizeof(float);
