@@ -106,6 +106,45 @@ __device__ __forceinline__ void store_chunk(char *row, const char *wrow, int64_t
     }
 }
 
+// The VEC elements of a full 16-byte chunk, widened to fp32.
+template <bool BF16>
+__device__ __forceinline__ void unpack_chunk(const uint4 &q, float *v)
+{
+    if constexpr (BF16) {
+        unpack8(q, v);
+    } else {
+        v[0] = __uint_as_float(q.x);
+        v[1] = __uint_as_float(q.y);
+        v[2] = __uint_as_float(q.z);
+        v[3] = __uint_as_float(q.w);
+    }
+}
+
+// A full chunk of y = round((x * rsq) * w), with w already loaded.
+template <bool BF16>
+__device__ __forceinline__ void store_full_chunk(char *row, int64_t c, const float *v,
+                                                 const float *w, float rsq)
+{
+    constexpr int VEC = Elt<BF16>::VEC;
+    float o[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+        o[e] = (v[e] * rsq) * w[e];
+    uint4 q;
+    if constexpr (BF16) {
+        q.x = pack_bf16x2(o[0], o[1]);
+        q.y = pack_bf16x2(o[2], o[3]);
+        q.z = pack_bf16x2(o[4], o[5]);
+        q.w = pack_bf16x2(o[6], o[7]);
+    } else {
+        q.x = __float_as_uint(o[0]);
+        q.y = __float_as_uint(o[1]);
+        q.z = __float_as_uint(o[2]);
+        q.w = __float_as_uint(o[3]);
+    }
+    *reinterpret_cast<uint4 *>(row + c * 16) = q;
+}
+
 // Fixed pairwise tree over the per-slot partials of one lane.
 template <int VEC>
 __device__ __forceinline__ float slot_tree(const float *p)
@@ -148,17 +187,38 @@ __global__ __launch_bounds__(64 * RPW) void rmsnorm_wave_kernel(const char *x, i
         part[e] = 0.f;
 
     if (nchunks <= 64 * CPL) {
+        // Every full chunk's x and w are requested up front with unconditional
+        // 16-byte loads (a lane past the last full chunk re-reads that chunk and
+        // discards it), so a row costs one memory latency, not one per chunk; the
+        // partial chunk at the end of a row whose length is not a multiple of VEC
+        // is read element by element.
+        const int64_t nfull = H / VEC;
+        const bool tail = nfull < nchunks;
+        const char *wr = w;
+        uint4 xq[CPL], wq[CPL];
+        if (nfull > 0) {
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int64_t c = min((int64_t)lane + 64 * i, nfull - 1);
+                xq[i] = *reinterpret_cast<const uint4 *>(xr + c * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int64_t c = min((int64_t)lane + 64 * i, nfull - 1);
+                wq[i] = *reinterpret_cast<const uint4 *>(wr + c * 16);
+            }
+        }
         float v[CPL][VEC];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int64_t c = lane + 64 * i;
-            if (c < nchunks) {
-                load_chunk<BF16>(xr, c, H, v[i]);
-            } else {
+            float t[VEC];
+            unpack_chunk<BF16>(xq[i], t);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    v[i][e] = 0.f;
-            }
+            for (int e = 0; e < VEC; ++e)
+                v[i][e] = c < nfull ? t[e] : 0.f;
+            if (tail && c == nfull)
+                load_chunk<BF16>(xr, c, H, v[i]);
         }
 #pragma unroll
         for (int i = 0; i < CPL; ++i)
@@ -169,8 +229,13 @@ __global__ __launch_bounds__(64 * RPW) void rmsnorm_wave_kernel(const char *x, i
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int64_t c = lane + 64 * i;
-            if (c < nchunks)
+            if (c < nfull) {
+                float wv[VEC];
+                unpack_chunk<BF16>(wq[i], wv);
+                store_full_chunk<BF16>(yr, c, v[i], wv, rsq);
+            } else if (tail && c == nfull) {
                 store_chunk<BF16>(yr, w, c, H, v[i], rsq);
+            }
         }
     } else {
         for (int64_t c = lane; c < nchunks; c += 64) {
@@ -209,6 +274,46 @@ __global__ __launch_bounds__(256) void rmsnorm_block_kernel(const char *x, int64
 #pragma unroll
     for (int e = 0; e < VEC; ++e)
         part[e] = 0.f;
+    constexpr int CPT = 4;  // chunks per thread held in registers (rows up to 1024 chunks)
+    const int64_t nfull = H / VEC;
+    if (nchunks <= 256 * CPT && nfull == nchunks) {
+        // every chunk full: x and w requested up front (clamped, unconditional
+        // 16-byte loads), one memory latency per row
+        uint4 xq[CPT], wq[CPT];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int64_t c = min((int64_t)t + 256 * i, nfull - 1);
+            xq[i] = *reinterpret_cast<const uint4 *>(xr + c * 16);
+            wq[i] = *reinterpret_cast<const uint4 *>(w + c * 16);
+        }
+        float v[CPT][VEC];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            float tmp[VEC];
+            unpack_chunk<BF16>(xq[i], tmp);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                v[i][e] = t + 256 * i < nfull ? tmp[e] : 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                part[e] = fmaf(v[i][e], v[i][e], part[e]);
+        }
+        const float s = wave_sum_butterfly(slot_tree<VEC>(part));
+        if ((t & 63) == 0)
+            wsum[t >> 6] = s;
+        __syncthreads();
+        const float rsq = inv_rms((wsum[0] + wsum[1]) + (wsum[2] + wsum[3]), H, eps);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int64_t c = t + 256 * i;
+            if (c < nfull) {
+                float wv[VEC];
+                unpack_chunk<BF16>(wq[i], wv);
+                store_full_chunk<BF16>(yr, c, v[i], wv, rsq);
+            }
+        }
+        return;
+    }
     for (int64_t c = t; c < nchunks; c += 256) {
         float v[VEC];
         load_chunk<BF16>(xr, c, H, v);
