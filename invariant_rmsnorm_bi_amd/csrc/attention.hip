@@ -429,12 +429,12 @@ __global__ __launch_bounds__(512, 4) void attn_split_kernel(
 // (consecutive prompt tokens).
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(
-    const float *__restrict__ ws_acc, const float *__restrict__ ws_ml,
+    const float *ws_acc, const float *ws_ml,
     const int32_t *__restrict__ kv_lens, int start, int64_t rows, int hq, int S, int max_kv_len,
     int nsmax, uint16_t *__restrict__ out, int64_t out_row_stride)
 {
     constexpr int EPL = D / 64;  // elements per lane
-    constexpr int UNROLL = 8;
+    constexpr int UNROLL = 16;
     const int lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (item >= rows * hq)
@@ -452,8 +452,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
         o[e] = 0.f;
     for (int s0 = 0; s0 < n; s0 += 64) {
         const int sl = s0 + lane;
-        const float m_l = sl < n ? ml[2 * sl] : -INFINITY;
-        const float l_l = sl < n ? ml[2 * sl + 1] : 0.f;
+        // unconditional loads (a lane past the last split re-reads it), selected after
+        const float2 ml_l = *reinterpret_cast<const float2 *>(ml + 2 * min(sl, n - 1));
+        const float m_l = sl < n ? ml_l.x : -INFINITY;
+        const float l_l = sl < n ? ml_l.y : 0.f;
         float Mi = m_l;  // max(M, m_s0 .. m_sl)
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -470,12 +472,21 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
         M = __shfl(Mi, 63, kWave);
         const int cnt = min(64, n - s0);
         for (int j0 = 0; j0 < cnt; j0 += UNROLL) {
+            // every load issued before the first use; past the row's last split a
+            // lane re-reads that split (its value is never folded)
             float a[UNROLL][EPL];
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    a[u][e] = (j0 + u < cnt) ? ac[(int64_t)(s0 + j0 + u) * D + e] : 0.f;
+            for (int u = 0; u < UNROLL; ++u) {
+                const float *src = ac + (int64_t)(s0 + min(j0 + u, cnt - 1)) * D;
+                if constexpr (EPL == 2) {
+                    const float2 t = *reinterpret_cast<const float2 *>(src);
+                    a[u][0] = t.x;
+                    a[u][1] = t.y;
+                } else {
+                    a[u][0] = src[0];
+                }
+            }
+            asm volatile("" ::: "memory");  // keep the batch of loads ahead of the folds
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 if (j0 + u < cnt) {
