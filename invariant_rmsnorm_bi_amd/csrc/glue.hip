@@ -81,8 +81,13 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi)
 }
 
 // One 1024-thread workgroup per row.
-__global__ __launch_bounds__(1024) void argmax_kernel(const float *__restrict__ x, int64_t xs,
-                                                      int64_t n, int32_t *__restrict__ out)
+// VEC4: the row is 16-byte aligned, so its full 4-element chunks are read as
+// float4, four per thread per step, all requested before any is compared (a
+// thread past the last chunk re-reads it and ignores the value); the elements
+// after the last full chunk are read one by one.
+template <bool VEC4>
+__global__ __launch_bounds__(1024) void argmax_kernel(const float *x, int64_t xs, int64_t n,
+                                                      int32_t *__restrict__ out)
 {
     __shared__ float sv[16];
     __shared__ int si[16];
@@ -90,7 +95,33 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float *__restrict__ 
     const float *row = x + r * xs;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int64_t i = threadIdx.x; i < n; i += 1024) {
+    int64_t scalar_from = 0;
+    if constexpr (VEC4) {
+        const int64_t n4 = n / 4;
+        const float4 *row4 = reinterpret_cast<const float4 *>(row);
+        for (int64_t base = 0; base < n4; base += 4 * 1024) {
+            float4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                v[k] = row4[min(base + k * 1024 + threadIdx.x, n4 - 1)];
+            asm volatile("" ::: "memory");  // all four loads in flight before the compares
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t c = base + k * 1024 + threadIdx.x;
+                if (c < n4) {
+                    const float e[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (e[j] == e[j] && better(e[j], (int)(4 * c + j), bv, bi)) {
+                            bv = e[j];
+                            bi = (int)(4 * c + j);
+                        }
+                }
+            }
+        }
+        scalar_from = 4 * n4;
+    }
+    for (int64_t i = scalar_from + threadIdx.x; i < n; i += 1024) {
         const float v = row[i];
         if (v == v && better(v, (int)i, bv, bi)) {
             bv = v;
@@ -153,7 +184,10 @@ hipError_t launch_swiglu(const uint16_t *gu, int64_t gs, uint16_t *out, int64_t 
 hipError_t launch_argmax(const float *x, int64_t xs, int64_t rows, int64_t n, int32_t *out,
                          hipStream_t s)
 {
-    argmax_kernel<<<dim3((unsigned)rows), dim3(1024), 0, s>>>(x, xs, n, out);
+    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0 && xs % 4 == 0)
+        argmax_kernel<true><<<dim3((unsigned)rows), dim3(1024), 0, s>>>(x, xs, n, out);
+    else
+        argmax_kernel<false><<<dim3((unsigned)rows), dim3(1024), 0, s>>>(x, xs, n, out);
     return hipGetLastError();
 }
 
