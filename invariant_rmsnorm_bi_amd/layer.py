@@ -26,7 +26,7 @@ import numpy as np
 import torch
 
 from . import (argmax_rows, decode_attn_bi, decode_attn_tuned, embed, kv_append, matmul_bi,
-               matmul_tuned, residual_add, rmsnorm_bi, rmsnorm_tuned, swiglu)
+               matmul_tuned, prefill_attn_bi, residual_add, rmsnorm_bi, rmsnorm_tuned, swiglu)
 
 
 @dataclass
@@ -80,6 +80,31 @@ class DecodeLayer:
             + positions % c.page_size
         return bt, slots.astype(np.int32), (positions + 1).astype(np.int32)
 
+    @staticmethod
+    def segments(bt: np.ndarray, positions) -> list:
+        """Split a step's rows into runs for attention: a run of at least two rows
+        that are consecutive positions of one request (one block-table row) is a
+        prompt chunk, attended by the prefill kernel; the other rows are decode
+        rows.  Returns [(first_row, end_row, chunk_start_position or -1)], in row
+        order; the prefill kernel gives each token its decode row's bits, so the
+        split changes speed only."""
+        positions = np.asarray(positions, dtype=np.int64)
+        B = positions.shape[0]
+        segs = []
+        i = 0
+        while i < B:
+            j = i + 1
+            while j < B and positions[j] == positions[j - 1] + 1 and np.array_equal(bt[j], bt[i]):
+                j += 1
+            if j - i >= 2:
+                segs.append((i, j, int(positions[i])))
+            elif segs and segs[-1][2] < 0:
+                segs[-1] = (segs[-1][0], j, -1)
+            else:
+                segs.append((i, j, -1))
+            i = j
+        return segs
+
     def step(self, tokens, block_table: np.ndarray, positions) -> tuple[torch.Tensor, torch.Tensor]:
         """Run rows (tokens[i] at positions[i] of the request whose block table is
         block_table[i]).  Returns (fp32 logits [B, vocab], argmax tokens [B] int32)."""
@@ -87,12 +112,15 @@ class DecodeLayer:
         bt, slots, lens_h = self.schedule(block_table, positions)
         tok = torch.as_tensor(np.asarray(tokens, dtype=np.int32)).to(dev, non_blocking=False)
         return self.forward(tok, torch.from_numpy(bt).to(dev), torch.from_numpy(slots).to(dev),
-                            torch.from_numpy(lens_h).to(dev), lens_h)
+                            torch.from_numpy(lens_h).to(dev), lens_h,
+                            segments=self.segments(bt, positions))
 
-    def forward(self, tok, bt_d, slots_d, lens_d, lens_h):
+    def forward(self, tok, bt_d, slots_d, lens_d, lens_h, segments=None):
         """The device part of a step on device inputs (token ids, block tables, cache
         slots, KV lengths); lens_h, the lengths on the host, only steers the twin's
-        split size."""
+        split size.  segments (from segments()) routes prompt chunks to the prefill
+        kernel; without it every row is a decode row.  The twin always runs every
+        row through its decode kernel."""
         c = self.cfg
         B = tok.shape[0]
         x = embed(self.w["embed"], tok)
@@ -105,9 +133,18 @@ class DecodeLayer:
         if self.tuned:
             o = decode_attn_tuned(q, self.k_cache, self.v_cache, bt_d, lens_d, c.max_kv_len,
                                   kv_lens_host=lens_h)
-        else:
+        elif segments is None or all(p < 0 for _, _, p in segments):
             o = decode_attn_bi(q, self.k_cache, self.v_cache, bt_d, lens_d, c.max_kv_len,
                                c.split_size)
+        else:
+            o = torch.empty((B, c.num_q_heads, c.head_dim), dtype=torch.bfloat16, device=tok.device)
+            for a, b, p0 in segments:
+                if p0 < 0:
+                    decode_attn_bi(q[a:b], self.k_cache, self.v_cache, bt_d[a:b], lens_d[a:b],
+                                   c.max_kv_len, c.split_size, out=o[a:b])
+                else:
+                    prefill_attn_bi(q[a:b], self.k_cache, self.v_cache, bt_d[a], p0,
+                                    c.split_size, out=o[a:b])
         y = self._mm(o.view(B, c.q_width), self.w["wo"])
         h = residual_add(x, y)
         a2 = self._norm(h, self.w["ln2"])

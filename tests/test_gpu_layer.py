@@ -210,6 +210,42 @@ def test_graph_replay_equals_eager_steps(weights):
 
 
 
+def test_prompt_chunks_through_prefill_equal_decode_rows(weights):
+    # A step whose rows mix decode rows of other requests with prompt chunks (runs
+    # of consecutive positions of one request) sends the chunks to the prefill
+    # kernel; its logits must equal, bit for bit, the same step with every row run
+    # as a decode row.  Chunks start at 0 and mid-prompt, one crosses the 256-token
+    # split boundary, and one request's chunk is split by a decode row.
+    rng = np.random.default_rng(23)
+    pages = 24
+    a_tab = _table(list(range(0, pages)))
+    b_tab = _table(list(range(pages, 2 * pages)))
+    d_tabs = [_table(list(range((2 + r) * pages, (3 + r) * pages))) for r in range(3)]
+    rows_tab = [d_tabs[0]] + [a_tab] * 70 + [d_tabs[1]] + [b_tab] * 5 + [d_tabs[2]] + [b_tab] * 3
+    rows_pos = [300] + list(range(220, 290)) + [5] + list(range(0, 5)) + [40] + list(range(5, 8))
+    B = len(rows_pos)
+    tok = rng.integers(0, CFG.vocab, B)
+    bt = np.stack(rows_tab)
+    segs = DecodeLayer.segments(bt, rows_pos)
+    assert [s for s in segs if s[2] >= 0] == [(1, 71, 220), (72, 77, 0), (78, 81, 5)]
+    out = {}
+    for mode in ("segments", "decode"):
+        layer = DecodeLayer(CFG, weights, num_pages=5 * pages)
+        kc = synth.normal(tuple(layer.k_cache.shape), seed=70, device=DEV)
+        layer.k_cache.copy_(kc)
+        layer.v_cache.copy_(synth.normal(tuple(layer.v_cache.shape), seed=71, device=DEV))
+        del kc
+        bt_, slots, lens_h = layer.schedule(bt, rows_pos)
+        args = (torch.as_tensor(tok.astype(np.int32)).to(DEV), torch.from_numpy(bt_).to(DEV),
+                torch.from_numpy(slots).to(DEV), torch.from_numpy(lens_h).to(DEV), lens_h)
+        lg, tk = layer.forward(*args, segments=segs if mode == "segments" else None)
+        torch.cuda.synchronize()
+        out[mode] = (lg.clone(), tk.clone())
+        del layer
+    assert torch.equal(out["segments"][0], out["decode"][0])
+    assert torch.equal(out["segments"][1], out["decode"][1])
+
+
 def test_seeded_sampling_reproducible_in_any_batch(weights):
     # non-greedy decoding (temperature 0.8, the probe's own seed) on top of the
     # invariant layer: the probe's sampled tokens are the same alone and inside
