@@ -174,7 +174,8 @@ int matmul_tuned(const void *A, int64_t lda, const void *W, int64_t ldw, void *C
  *               splits s >= ceil(kv_lens[r] / split_size) are not written
  * Supported: head_dim 64 or 128; page_size 16; split_size a positive multiple of
  * page_size, at most 1024; num_q_heads % num_kv_heads == 0 with a group of 1..16
- * query heads;
+ * query heads; rows <= 65535 and ceil(max_kv_len / split_size) * num_kv_heads
+ * < 2^31;
  * q, out 16-byte aligned with row strides multiples of 8.  A kv_lens entry
  * outside [1, max_kv_len] is clamped into that range on the device (it cannot
  * be reported from there); keep lengths valid.

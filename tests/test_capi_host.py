@@ -112,6 +112,11 @@ def test_decode_attn_validation():
     need = rbi.decode_attn_workspace_size(4, 64, 128, 32768, 256)
     assert need == 4 * 64 * 128 * 130 * 4     # 128 splits of 256
     assert _attn(wsb=need - 1) == EWORKSPACE
+    # grid bounds: rows <= 65535 and (splits per row) * kv heads < 2^31
+    assert _attn(rows=65536) == EUNSUPPORTED
+    big = dict(maxlen=(1 << 31) - 1, split=16, bts=1 << 27)   # 2^27 splits per row
+    assert _attn(hq=16, hkv=16, **big) == EUNSUPPORTED
+    assert _attn(hq=16, hkv=8, **big) == EWORKSPACE           # 2^30 grid columns: in bounds
 
 
 def test_decode_attn_workspace_depends_only_on_bounds():
