@@ -16,7 +16,9 @@ rotate over 4 buffer sets (> 512 MB) so the 256 MB last-level cache does not
 serve them warm.  ``value`` = algorithmic HBM bytes of the step / step time.
 
 Printed: ONE JSON line with the metric, a per-kernel breakdown (HBM GB/s or MFMA
-TFLOP/s against the chip's peak), the ``roofline`` object of the dominant kernel
+TFLOP/s against the chip's peak; for the two projections also the vendor GEMM,
+hipBLASLt through torch.matmul, timed interleaved on the same operands as
+context), the ``roofline`` object of the dominant kernel
 (decode attention), the shape-tuned twins' times and the determinism slowdown
 (t_bi / t_tuned - 1), prefill attention against the same tokens as decode rows,
 and the CPU oracle timed on a bounded sample of the same
@@ -162,6 +164,31 @@ def time_fn(fn, reps=20, warm=3):
         b.synchronize()
         ts.append(a.elapsed_time(b))
     return float(np.median(ts))
+
+
+def vendor_gemm_us(wl: Workload):
+    """Context only: the vendor GEMM (hipBLASLt, reached through torch.matmul) on the
+    step's two projections with the same rotating operand sets, timed interleaved
+    with matmul_bi.  Median device us per call, {name: (bi_us, vendor_us)}."""
+    out = {}
+    for name, a_sets, w_sets, c in (("matmul_bi_qkv", wl.a_qkv, wl.w_qkv, wl.c_qkv),
+                                    ("matmul_bi_oproj", wl.a_o, wl.w_o, wl.c_o)):
+        fns = {"bi": lambda s: rbi.matmul_bi(a_sets[s], w_sets[s], out=c),
+               "vendor": lambda s: torch.matmul(a_sets[s], w_sets[s].t(), out=c)}
+        ts = {k: [] for k in fns}
+        for i in range(3):
+            for f in fns.values():
+                f(i % SETS)
+        for i in range(20):
+            for k, f in fns.items():
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                f(i % SETS)
+                b.record()
+                b.synchronize()
+                ts[k].append(a.elapsed_time(b) * 1e3)
+        out[name] = (float(np.median(ts["bi"])), float(np.median(ts["vendor"])))
+    return out
 
 
 def twin_points(wl: Workload):
@@ -518,6 +545,9 @@ def main():
 
     twins = None
     if not args.no_twins:
+        log("timing the vendor GEMM on the step's projections (context)")
+        for n, (tb, tv) in vendor_gemm_us(wl).items():
+            kernels[n].update({"interleaved_us": round(tb, 2), "vendor_gemm_us": round(tv, 2)})
         log("timing the tuned twins")
         pts = []
         for name, fbi, ftu in twin_points(wl):
