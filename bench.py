@@ -57,6 +57,22 @@ OPROJ = (4096, 8192)
 ATT_B, HQ, HKV, D, PAGE, SPLIT, LMAX = 256, 64, 4, 128, 16, 256, 32768
 SETS = 4
 
+# The cost of determinism as the pages report it ("Reproducible LLM Inference ...",
+# hidekazu-konishi.com, sections 8.2 and 8.3): end-to-end serving time on NVIDIA
+# hardware, other models and workloads.  Context only, never a target; the unit is
+# the increase in time, as above.
+PAGES_COST_CONTEXT = {
+    "thinking_machines_seconds": {
+        "workload": "Qwen-3-8B API server, 1000 sequences of 90-110 output tokens, one GPU "
+                    "(model not stated)",
+        "default": 26, "deterministic_unoptimised": 55, "deterministic_better_attention": 42},
+    "sglang_slowdown_pct": {
+        "workload": "Qwen3-8B, TP1, H200 (140 GB), three rollout workloads of 256 requests, "
+                    "radix cache off",
+        "mean_flashinfer_fa3": 34.35, "range": [24.4, 55.1]},
+    "source": "hidekazu-konishi.com, Reproducible LLM Inference, sections 8.2-8.3",
+}
+
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
@@ -556,7 +572,8 @@ def main():
                         "slowdown_pct": round((tb / tt - 1) * 100, 2)})
         mean = float(np.mean([p["slowdown_pct"] for p in pts]))
         twins = {"points": pts, "mean_slowdown_pct": round(mean, 2),
-                 "unit": "time increase of bi over tuned, percent"}
+                 "unit": "time increase of bi over tuned, percent",
+                 "pages_context": PAGES_COST_CONTEXT}
         if not args.no_layer:
             log("timing the decode layer, bi against tuned")
             lp = layer_points()
