@@ -167,25 +167,32 @@ class Workload:
 # timing helpers
 # --------------------------------------------------------------------------------------
 
-def time_fn(fn, reps=20, warm=3):
-    """Median device time (ms) of fn over reps, hipEvents on the current stream."""
+def time_fn(fn, reps=20, warm=3, inner=10):
+    """Median device time (ms) of one call of fn, hipEvents on the current stream.
+    Each sample queues `inner` calls back to back behind one untimed call, so the
+    host's per-call cost (argument marshalling, launch) overlaps the device work
+    instead of leaving the GPU idle between the events."""
     for _ in range(warm):
         fn()
+    torch.cuda.synchronize()
     ts = []
     for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
         fn()
+        a.record()
+        for _ in range(inner):
+            fn()
         b.record()
         b.synchronize()
-        ts.append(a.elapsed_time(b))
+        ts.append(a.elapsed_time(b) / inner)
     return float(np.median(ts))
 
 
 def vendor_gemm_us(wl: Workload):
     """Context only: the vendor GEMM (hipBLASLt, reached through torch.matmul) on the
     step's two projections with the same rotating operand sets, timed interleaved
-    with matmul_bi.  Median device us per call, {name: (bi_us, vendor_us)}."""
+    with matmul_bi (each sample: SETS calls queued back to back, one per operand
+    set, behind an untimed call).  Median device us per call, {name: (bi_us, vendor_us)}."""
     out = {}
     for name, a_sets, w_sets, c in (("matmul_bi_qkv", wl.a_qkv, wl.w_qkv, wl.c_qkv),
                                     ("matmul_bi_oproj", wl.a_o, wl.w_o, wl.c_o)):
@@ -195,14 +202,17 @@ def vendor_gemm_us(wl: Workload):
         for i in range(3):
             for f in fns.values():
                 f(i % SETS)
-        for i in range(20):
+        torch.cuda.synchronize()
+        for i in range(10):
             for k, f in fns.items():
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                f(SETS - 1)
                 a.record()
-                f(i % SETS)
+                for s in range(SETS):
+                    f(s)
                 b.record()
                 b.synchronize()
-                ts[k].append(a.elapsed_time(b) * 1e3)
+                ts[k].append(a.elapsed_time(b) * 1e3 / SETS)
         out[name] = (float(np.median(ts["bi"])), float(np.median(ts["vendor"])))
     return out
 

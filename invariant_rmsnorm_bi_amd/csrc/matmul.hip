@@ -434,6 +434,125 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     }
 }
 
+// One-wave weight-streaming tile for small M (K a multiple of 32): TBM batch rows x
+// 16 features per wave, one wave per workgroup.  A single wave shares nothing through
+// LDS, so the operand fragments go straight from global memory into a register ring
+// of P steps: each lane loads exactly the 16 bytes it feeds to the MFMA (row lane % 16,
+// k = 8 * (lane / 16) .. +7 of the step), P steps ahead of their use.  A step is then
+// one MFMA per 16-row block and one load per operand, with no barrier and no LDS round
+// trip.  Instruction, operand roles, k fragment mapping and the ascending step order
+// are those of mm_tile_kernel and mm_pipe_kernel, so every element gets the same bits.
+// Rows past M or N read a valid row whose results are never stored; the ring's refills
+// past the last step re-read that step (in bounds) and are never used.
+template <int TBM, int P, bool OUT_BF16>
+__global__ __launch_bounds__(64) void mm_stream_kernel(
+    const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restrict__ W, int64_t ldw,
+    void *__restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n,
+    int64_t k_split, int64_t c_split_stride)
+{
+    {  // split-K (blockIdx.y = range; the invariant path always has one range)
+        const int64_t kb0 = (int64_t)blockIdx.y * k_split;
+        A += kb0;
+        W += kb0;
+        K = (int)((K - kb0) < k_split ? (K - kb0) : k_split);
+        C = reinterpret_cast<char *>(C) + (int64_t)blockIdx.y * c_split_stride;
+    }
+    constexpr int FM = TBM / 16;
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, BIG_GROUP_M, tm, tn);
+    const int m0 = tm * TBM, n0 = tn * 16;
+    const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+
+    const uint16_t *wp = W + (int64_t)min(n0 + lr, N - 1) * ldw + 8 * lq;
+    const uint16_t *ap[FM];
+#pragma unroll
+    for (int b = 0; b < FM; ++b)
+        ap[b] = A + (int64_t)min(m0 + b * 16 + lr, M - 1) * lda + 8 * lq;
+
+    const int nk = K / PK;
+    uint4 rw[P], ra[P][FM];
+    auto load = [&](int slot, int step) {
+        const int st = min(step, nk - 1);
+        rw[slot] = *reinterpret_cast<const uint4 *>(wp + (int64_t)st * PK);
+#pragma unroll
+        for (int b = 0; b < FM; ++b)
+            ra[slot][b] = *reinterpret_cast<const uint4 *>(ap[b] + (int64_t)st * PK);
+    };
+    f32x4_t acc[FM];
+#pragma unroll
+    for (int b = 0; b < FM; ++b)
+        acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto step = [&](int slot) {
+#pragma unroll
+        for (int b = 0; b < FM; ++b)
+            acc[b] = mfma_16x16x32_bf16(as_bf16x8(rw[slot]), as_bf16x8(ra[slot][b]), acc[b]);
+    };
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        load(j, j);
+    // Steady rounds are branch free, so the compiler's load-counter waits stay exact
+    // (each step waits only for its own slot); the last partial round has no refills.
+    int kt = 0;
+    for (; kt + P <= nk; kt += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            step(j);
+            load(j, kt + j + P);
+        }
+        // keep each refill right behind the MFMAs that free its slot (instruction
+        // classes: 0x8 MFMA, 0x20 global load), rather than batched at the round's end
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1 + FM, 0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        if (kt + j < nk)
+            step(j);
+
+    // lane holds batch row m = lane % 16 of each block and features n = 4*(lane/16) + j
+    const int n = n0 + 4 * lq;
+    if (n >= N)
+        return;
+#pragma unroll
+    for (int b = 0; b < FM; ++b) {
+        const int m = m0 + b * 16 + lr;
+        if (m >= M)
+            continue;
+        const f32x4_t v = acc[b];
+        if constexpr (OUT_BF16) {
+            uint2 o;
+            o.x = pack_bf16x2(v[0], v[1]);
+            o.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(C) + (int64_t)m * ldc + n) = o;
+        } else {
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(C) + (int64_t)m * ldc + n) =
+                make_float4(v[0], v[1], v[2], v[3]);
+        }
+    }
+}
+
+template <int TBM, int P>
+hipError_t launch_stream(const MatmulArgs &a, hipStream_t s, int splits = 1, int64_t k_split = 0,
+                         int64_t c_split_stride = 0)
+{
+    if (splits == 1)
+        k_split = a.K;
+    const int tiles_m = (int)((a.M + TBM - 1) / TBM), tiles_n = (int)((a.N + 15) / 16);
+    const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits), block(64);
+    if (a.c_bf16)
+        mm_stream_kernel<TBM, P, true><<<grid, block, 0, s>>>(
+            a.A, a.lda, a.W, a.ldw, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_m, tiles_n,
+            k_split, c_split_stride);
+    else
+        mm_stream_kernel<TBM, P, false><<<grid, block, 0, s>>>(
+            a.A, a.lda, a.W, a.ldw, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_m, tiles_n,
+            k_split, c_split_stride);
+    return hipGetLastError();
+}
+
 hipError_t launch_tiles(const MatmulArgs &a, int splits, int64_t k_split, void *C, int64_t ldc,
                         bool out_bf16, int64_t c_split_stride, hipStream_t s)
 {
@@ -460,9 +579,10 @@ struct TileCand {
 };
 constexpr TileCand kTiles[] = {{256, 256, 0.56}, {256, 128, 0.42}, {128, 128, 0.39},
                                {128, 64, 0.20},  {64, 64, 0.15},   {64, 32, 0.10},
-                               {16, 16, 0.0},    {32, 16, 0.0}};
-constexpr int kNumTiles = 6;  // priced by the cost model; the last two are one-wave
-                              // weight-streaming tiles for small M (rule below)
+                               {16, 16, 0.0},    {32, 16, 0.0},    {16, 16, 0.0}};
+constexpr int kNumTiles = 6;  // priced by the cost model; the last three are one-wave
+                              // weight-streaming tiles for small M (rule below): 16 x 16
+                              // and 32 x 16 through LDS, and 16 x 16 in registers
 
 // (rounds of 256 workgroups) x (tile area) / (throughput per unit area)
 double tile_cost(int i, int64_t M, int64_t N)
@@ -475,11 +595,22 @@ double tile_cost(int i, int64_t M, int64_t N)
 int best_tile(int64_t M, int64_t N, double *cost)
 {
     // Small M is a weight stream: one-wave 16-row tiles give every compute unit
-    // several independent streams.  16 x 16 while there are at most 1024 of them,
-    // else 32 x 16 up to M = 32 (measured on the attention projections).
+    // several independent streams.  Measured on MI355X (decode-layer weights):
+    //  * at most one 16 x 16 tile per compute unit (N <= 4096): a wave's stream is
+    //    latency bound, and the register-streaming kernel, free of the LDS round
+    //    trip and barrier of every step, is faster up to M = 16 (o_proj M = 1:
+    //    20.6 -> 14.0 us, down projection 28.4 -> 18.7 us); with more tiles per
+    //    unit the LDS kernels are as fast or faster (QKV M = 1: 16.9 vs 18.7 us);
+    //  * otherwise 16 x 16 through LDS while there are at most 1024 of them, and
+    //    for vocabulary-sized N up to M = 8 (lm_head M = 1: 217.9 -> 204.8 us);
+    //  * else 32 x 16 up to M = 32.
     if (M <= 64) {
         const int64_t t16 = ((M + 15) / 16) * ((N + 15) / 16);
-        if (t16 <= 1024) {
+        if (M <= 16 && t16 <= 256) {
+            *cost = 0;
+            return 8;
+        }
+        if (t16 <= 1024 || (M <= 8 && t16 > 2048)) {
             *cost = 0;
             return 6;
         }
@@ -512,7 +643,8 @@ hipError_t launch_tile_shape(int i, const MatmulArgs &a, hipStream_t s, int spli
     case 4: return launch_pipe<64, 64, 2, 2, 8>(a, s, splits, k_split, c_split_stride);
     case 5: return launch_pipe<64, 32, 2, 1, 16>(a, s, splits, k_split, c_split_stride);
     case 6: return launch_pipe<16, 16, 1, 1, 16>(a, s, splits, k_split, c_split_stride);
-    default: return launch_pipe<32, 16, 1, 1, 16>(a, s, splits, k_split, c_split_stride);
+    case 7: return launch_pipe<32, 16, 1, 1, 16>(a, s, splits, k_split, c_split_stride);
+    default: return launch_stream<16, 12>(a, s, splits, k_split, c_split_stride);
     }
 }
 
@@ -586,7 +718,10 @@ int matmul_tuned_splits(int64_t M, int64_t N, int64_t K)
         const int ti = best_tile(M, N, &c);
         const TileCand &t = kTiles[ti];
         tiles = ((M + t.tbm - 1) / t.tbm) * ((N + t.tbn - 1) / t.tbn);
-        if (ti >= kNumTiles) {
+        if (ti == 8) {
+            return 1;  // the register-streaming tile: split-K over it measured slower
+                       // (o_proj M = 1: 15.4 us in 4 ranges vs 11.2 us unsplit)
+        } else if (ti >= kNumTiles) {
             target = 1024;  // one-wave weight-streaming tiles: ~4 per compute unit
         } else if (tiles > 128) {
             // multi-wave tiles filling at least half of the compute units: the fp32

@@ -70,16 +70,18 @@ def test_matmul_validation():
     assert f(FAKE, 64, FAKE, 64, FAKE + 8, 64, 1, 4, 64, 64, NULL) == EINVAL
     assert f(FAKE, 64, FAKE, 64, FAKE, 32, 1, 4, 64, 64, NULL) == EINVAL  # ldc < N
     g = rbi.lib().matmul_tuned
-    need = rbi.matmul_tuned_workspace_size(1, 4096, 8192)
+    need = rbi.matmul_tuned_workspace_size(1, 9216, 4096)
     assert need > 0
-    assert g(FAKE, 8192, FAKE, 8192, FAKE, 4096, 1, 1, 4096, 8192, NULL, need, NULL) == EWORKSPACE
-    assert g(FAKE, 8192, FAKE, 8192, FAKE, 4096, 1, 1, 4096, 8192, FAKE, need - 1, NULL) == EWORKSPACE
+    assert g(FAKE, 4096, FAKE, 4096, FAKE, 9216, 1, 1, 9216, 4096, NULL, need, NULL) == EWORKSPACE
+    assert g(FAKE, 4096, FAKE, 4096, FAKE, 9216, 1, 1, 9216, 4096, FAKE, need - 1, NULL) == EWORKSPACE
 
 
 def test_matmul_tuned_workspace_shape_dependence():
-    # the twin splits K only when the output tiles cannot fill the chip
+    # the twin splits K only when the output tiles cannot fill the chip, and not
+    # over the register-streaming tile (at most one 16 x 16 tile per compute unit)
     assert rbi.matmul_tuned_workspace_size(4096, 9216, 4096) == 0
-    assert rbi.matmul_tuned_workspace_size(1, 4096, 8192) > 0
+    assert rbi.matmul_tuned_workspace_size(1, 9216, 4096) > 0
+    assert rbi.matmul_tuned_workspace_size(1, 4096, 8192) == 0
     assert rbi.matmul_tuned_workspace_size(0, 9216, 4096) == 0
 
 

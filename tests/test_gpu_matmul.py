@@ -127,14 +127,17 @@ def test_p1_batch_slice_example():
     one = rbi.matmul_bi(a[:1], W, out_dtype=torch.float32)
     full = rbi.matmul_bi(a, W, out_dtype=torch.float32)[:1]
     assert float((one - full).abs().max()) == 0.0
-    # the split-K twin is free to change with the batch: it splits K at M = 1 only
-    t_one = rbi.matmul_tuned(a[:1], W, out_dtype=torch.float32)
-    t_full = rbi.matmul_tuned(a, W, out_dtype=torch.float32)[:1]
+    # the split-K twin is free to change with the batch: it splits K at M = 1 only.
+    # (At N = 4096 and M = 1 it runs the unsplit register-streaming tile, the same
+    # bits as matmul_bi, so the twin is shown on a linspace W twice as wide.)
+    W2 = synth.linspace_matrix(D, 2 * D, dtype=torch.bfloat16).T.contiguous().to(DEV)
+    t_one = rbi.matmul_tuned(a[:1], W2, out_dtype=torch.float32)
+    t_full = rbi.matmul_tuned(a, W2, out_dtype=torch.float32)[:1]
     assert float((t_one - t_full).abs().max()) > 0.0, "inputs lack the power to show a change"
 
 
 def test_tuned_twin_sensitivity_normal_inputs():
-    N, K = OPROJ
+    N, K = QKV  # the twin splits K at M = 1 here (not at o_proj's N = 4096)
     pool = synth.normal((4096, K), seed=41).to(DEV)
     W = synth.normal((N, K), std=0.02, seed=synth.SEED_WEIGHTS).to(DEV)
     small = rbi.matmul_tuned(pool[:1], W, out_dtype=torch.float32)
