@@ -4,8 +4,9 @@
 //
 // Batch invariance ("Reproducible LLM Inference ...", hidekazu-konishi.com,
 // section 5.3: give each batch element its own core so its reduction never
-// splits): every row is reduced by exactly one wavefront, in an order that is
-// a function of H alone.
+// splits): every row is reduced in one order that is a function of H alone --
+// that of a single wavefront, below -- whether one wave or several share the
+// row's loads and stores.
 //
 // Reduction order of one row (the contract of rmsnorm_bi):
 //   * the row is cut into 16-byte chunks (8 bf16 or 4 fp32 elements);
@@ -254,6 +255,92 @@ __global__ __launch_bounds__(64 * RPW) void rmsnorm_wave_kernel(const char *x, i
     }
 }
 
+// The wave-per-row arithmetic with the row's memory traffic spread over NWV waves,
+// for small batches (one row per workgroup): a single wave issues every load and
+// store of its row in sequence, which leaves a mostly idle chip waiting on one
+// wave per row.  Here wave v loads and stores the chunks of steps i = v*CPL/NWV ..
+// of every lane (lane l, step i: chunk l + 64 i, as in rmsnorm_wave_kernel), parks
+// their fp32 values in LDS, and after one barrier every wave reduces the whole row
+// exactly as the single wave does: lane l's slot partials over its chunks in
+// ascending step order, the slot tree and the butterfly.  Each wave then writes its
+// own chunks with that rsq.  Rows of at most 64 * CPL chunks.
+template <bool BF16, int CPL, int NWV>
+__global__ __launch_bounds__(64 * NWV) void rmsnorm_split_kernel(const char *x, int64_t xs,
+                                                                 const char *__restrict__ w,
+                                                                 char *y, int64_t ys,
+                                                                 int64_t rows, int64_t H,
+                                                                 float eps)
+{
+    constexpr int VEC = Elt<BF16>::VEC;
+    constexpr int SZ = Elt<BF16>::SIZE;
+    constexpr int SPW = CPL / NWV;  // steps per wave
+    static_assert(CPL % NWV == 0, "steps per wave");
+    __shared__ float vs[CPL * VEC][64];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int64_t row = blockIdx.x;
+    const char *xr = x + row * xs * SZ;
+    char *yr = y + row * ys * SZ;
+    const int64_t nchunks = (H + VEC - 1) / VEC;
+    const int64_t nfull = H / VEC;
+    const bool tail = nfull < nchunks;
+
+    uint4 xq[SPW], wq[SPW];
+    if (nfull > 0) {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            const int64_t c = min((int64_t)lane + 64 * (wv * SPW + j), nfull - 1);
+            xq[j] = *reinterpret_cast<const uint4 *>(xr + c * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            const int64_t c = min((int64_t)lane + 64 * (wv * SPW + j), nfull - 1);
+            wq[j] = *reinterpret_cast<const uint4 *>(w + c * 16);
+        }
+    }
+    float v[SPW][VEC];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        const int i = wv * SPW + j;
+        const int64_t c = lane + 64 * i;
+        float t[VEC];
+        unpack_chunk<BF16>(xq[j], t);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            v[j][e] = c < nfull ? t[e] : 0.f;
+        if (tail && c == nfull)
+            load_chunk<BF16>(xr, c, H, v[j]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            vs[i * VEC + e][lane] = v[j][e];
+    }
+    __syncthreads();
+
+    float part[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+        part[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float a = vs[i * VEC + e][lane];
+            part[e] = fmaf(a, a, part[e]);
+        }
+    const float rsq = inv_rms(wave_sum_butterfly(slot_tree<VEC>(part)), H, eps);
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        const int64_t c = lane + 64 * (wv * SPW + j);
+        if (c < nfull) {
+            float wv8[VEC];
+            unpack_chunk<BF16>(wq[j], wv8);
+            store_full_chunk<BF16>(yr, c, v[j], wv8, rsq);
+        } else if (tail && c == nfull) {
+            store_chunk<BF16>(yr, w, c, H, v[j], rsq);
+        }
+    }
+}
+
 // Twin: one 256-thread workgroup per row.  Thread t owns chunks t, t+256, ...;
 // slot tree, wave butterfly, then the four wave sums ((w0 + w1) + (w2 + w3)).
 template <bool BF16>
@@ -339,8 +426,15 @@ hipError_t launch_rmsnorm_wave(const void *x, int64_t xs, const void *w, void *y
                                int64_t rows, int64_t hidden, float eps, bool bf16,
                                hipStream_t s)
 {
-    // the workgroup size changes with the batch, never a row's arithmetic
-    if (rows >= 4096) {
+    // The workgroup shape changes with the batch, never a row's arithmetic.
+    // Measured on MI355X with H = 4096 bf16 (device time of graph-replayed calls):
+    // up to 256 rows, eight waves per row (3.0-3.6 us; one wave per row 5.2-5.7 us);
+    // up to 2047 rows, four (1024 rows: 6.0 vs 7.1 us); from 2048 rows on, one wave
+    // per row and four rows per workgroup.  Rows longer than 64 * 8 chunks always
+    // take the wave kernel's two-pass path.
+    const int64_t vec = bf16 ? 8 : 4;
+    const bool in_regs = (hidden + vec - 1) / vec <= 64 * 8;
+    if (rows >= 2048 || (!in_regs && rows >= 4096)) {
         const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
         if (bf16)
             rmsnorm_wave_kernel<true, 8, 4><<<grid, block, 0, s>>>(
@@ -348,13 +442,29 @@ hipError_t launch_rmsnorm_wave(const void *x, int64_t xs, const void *w, void *y
         else
             rmsnorm_wave_kernel<false, 8, 4><<<grid, block, 0, s>>>(
                 (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
-    } else {
+    } else if (!in_regs) {
         const dim3 grid((unsigned)rows), block(64);
         if (bf16)
             rmsnorm_wave_kernel<true, 8, 1><<<grid, block, 0, s>>>(
                 (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
         else
             rmsnorm_wave_kernel<false, 8, 1><<<grid, block, 0, s>>>(
+                (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
+    } else if (rows <= 256) {
+        const dim3 grid((unsigned)rows), block(512);
+        if (bf16)
+            rmsnorm_split_kernel<true, 8, 8><<<grid, block, 0, s>>>(
+                (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
+        else
+            rmsnorm_split_kernel<false, 8, 8><<<grid, block, 0, s>>>(
+                (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
+    } else {
+        const dim3 grid((unsigned)rows), block(256);
+        if (bf16)
+            rmsnorm_split_kernel<true, 8, 4><<<grid, block, 0, s>>>(
+                (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
+        else
+            rmsnorm_split_kernel<false, 8, 4><<<grid, block, 0, s>>>(
                 (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
     }
     return hipGetLastError();
