@@ -289,9 +289,10 @@ def layer_points():
     SwiGLU 12288, lm_head 151936, greedy argmax) built from the bi kernels versus
     the same layer built from the tuned twins, at batch sizes 1, 16, 64 and 128;
     each request has its own pages and a KV length ~ U{1..4096} (the cache holds
-    seeded random K/V).  Wall clock per step (host scheduling included, the same
-    for both), median of 10 after 3 warmup steps; also the bi step replayed as a
-    captured HIP graph (same kernels, no per-launch host cost)."""
+    seeded random K/V).  Wall clock per step (host scheduling included), median of
+    10 after 3 warmup steps, eager and replayed as a captured HIP graph (same
+    kernels, no per-launch host cost); the graphed pair prices determinism on the
+    device work, the eager pair includes each side's host cost."""
     from invariant_rmsnorm_bi_amd.layer import DecodeLayer, GraphedStep, LayerConfig
     cfg = LayerConfig()
     w = synth.dense_layer_weights(cfg.hidden, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
@@ -328,23 +329,26 @@ def layer_points():
                 torch.cuda.synchronize()
                 ts.append(time.perf_counter() - t0)
             t[tuned] = float(np.median(ts)) * 1e6
-        # the bi step captured as a HIP graph: same kernels, no per-launch host cost
-        g = GraphedStep(layers[False], table[:B], pos[:B], toks[:B])
-        for _ in range(3):
-            g.step(toks[:B], pos[:B])
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(10):
-            t0 = time.perf_counter()
-            g.step(toks[:B], pos[:B])
+        # each step captured as a HIP graph: same kernels, no per-launch host cost
+        tg = {}
+        for tuned in (False, True):
+            g = GraphedStep(layers[tuned], table[:B], pos[:B], toks[:B])
+            for _ in range(3):
+                g.step(toks[:B], pos[:B])
             torch.cuda.synchronize()
-            ts.append(time.perf_counter() - t0)
-        t_graph = float(np.median(ts)) * 1e6
-        del g
+            ts = []
+            for _ in range(10):
+                t0 = time.perf_counter()
+                g.step(toks[:B], pos[:B])
+                torch.cuda.synchronize()
+                ts.append(time.perf_counter() - t0)
+            tg[tuned] = float(np.median(ts)) * 1e6
+            del g
         pts.append({"point": f"layer step B={B}", "bi_us": round(t[False], 1),
                     "tuned_us": round(t[True], 1),
                     "slowdown_pct": round((t[False] / t[True] - 1) * 100, 2),
-                    "bi_graph_us": round(t_graph, 1)})
+                    "bi_graph_us": round(tg[False], 1), "tuned_graph_us": round(tg[True], 1),
+                    "graph_slowdown_pct": round((tg[False] / tg[True] - 1) * 100, 2)})
     del layers, w
     torch.cuda.empty_cache()
     return pts
@@ -620,7 +624,9 @@ def main():
             log("timing the decode layer, bi against tuned")
             lp = layer_points()
             twins["layer"] = {"points": lp, "mean_slowdown_pct": round(
-                float(np.mean([p["slowdown_pct"] for p in lp])), 2)}
+                float(np.mean([p["slowdown_pct"] for p in lp])), 2),
+                "mean_graph_slowdown_pct": round(
+                float(np.mean([p["graph_slowdown_pct"] for p in lp])), 2)}
 
     prefill = None
     if not args.no_prefill:

@@ -51,6 +51,43 @@ class LayerConfig:
         return self.num_kv_heads * self.head_dim
 
 
+class _Upload:
+    """A step's int32 inputs (token ids, block tables, cache slots, lengths) packed
+    into one pinned host buffer and moved by one asynchronous copy on the current
+    stream, instead of one synchronous copy from pageable memory per input.  Each
+    input starts on a 256-byte boundary.  The host buffer is rewritten only once the
+    previous copy out of it has finished; the device buffer is reused in stream
+    order, after the kernels of the previous step."""
+
+    ALIGN = 64  # int32 elements
+
+    def __init__(self, device):
+        self.device = device
+        self.host = None
+        self.dev = None
+        self.copied = None
+
+    def put(self, arrays):
+        arrays = [np.ascontiguousarray(a, dtype=np.int32) for a in arrays]
+        offs, n = [], 0
+        for a in arrays:
+            offs.append(n)
+            n += -(-a.size // self.ALIGN) * self.ALIGN
+        if self.host is None or self.host.numel() < n:
+            self.host = torch.empty(n, dtype=torch.int32, pin_memory=True)
+            self.dev = torch.empty(n, dtype=torch.int32, device=self.device)
+            self.copied = None
+        if self.copied is not None:
+            self.copied.synchronize()
+        h = self.host.numpy()
+        for a, o in zip(arrays, offs):
+            h[o: o + a.size] = a.reshape(-1)
+        self.dev[:n].copy_(self.host[:n], non_blocking=True)
+        self.copied = torch.cuda.Event()
+        self.copied.record()
+        return [self.dev[o: o + a.size].view(a.shape) for a, o in zip(arrays, offs)]
+
+
 class DecodeLayer:
     def __init__(self, cfg: LayerConfig, weights: dict, num_pages: int, device="cuda",
                  tuned: bool = False):
@@ -62,6 +99,7 @@ class DecodeLayer:
                                    dtype=torch.bfloat16, device=device)
         self.v_cache = torch.zeros((num_pages, cfg.num_kv_heads, cfg.head_dim, cfg.page_size),
                                    dtype=torch.bfloat16, device=device)
+        self._upload = _Upload(device)
 
     def _mm(self, a, w, out_dtype=torch.bfloat16):
         return (matmul_tuned if self.tuned else matmul_bi)(a, w, out_dtype=out_dtype)
@@ -108,11 +146,9 @@ class DecodeLayer:
     def step(self, tokens, block_table: np.ndarray, positions) -> tuple[torch.Tensor, torch.Tensor]:
         """Run rows (tokens[i] at positions[i] of the request whose block table is
         block_table[i]).  Returns (fp32 logits [B, vocab], argmax tokens [B] int32)."""
-        dev = self.device
         bt, slots, lens_h = self.schedule(block_table, positions)
-        tok = torch.as_tensor(np.asarray(tokens, dtype=np.int32)).to(dev, non_blocking=False)
-        return self.forward(tok, torch.from_numpy(bt).to(dev), torch.from_numpy(slots).to(dev),
-                            torch.from_numpy(lens_h).to(dev), lens_h,
+        tok, bt_d, slots_d, lens_d = self._upload.put([np.asarray(tokens), bt, slots, lens_h])
+        return self.forward(tok, bt_d, slots_d, lens_d, lens_h,
                             segments=self.segments(bt, positions))
 
     def forward(self, tok, bt_d, slots_d, lens_d, lens_h, segments=None):
@@ -171,9 +207,9 @@ class GraphedStep:
         bt, slots, lens_h = layer.schedule(block_table, positions)
         self.bt_h = bt
         self.bt = torch.from_numpy(bt).to(dev)
-        self.tok = torch.as_tensor(np.asarray(tokens, dtype=np.int32)).to(dev)
-        self.slots = torch.from_numpy(slots).to(dev)
-        self.lens = torch.from_numpy(lens_h).to(dev)
+        # per-replay inputs: one fixed device buffer, refilled by one copy per step
+        self._upload = _Upload(dev)
+        self.tok, self.slots, self.lens = self._upload.put([np.asarray(tokens), slots, lens_h])
         self.lens_h = lens_h
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -191,9 +227,7 @@ class GraphedStep:
         """Replay with new tokens and positions (same rows, same block tables).
         Returns the captured output buffers (overwritten by the next replay)."""
         _, slots, lens_h = self.layer.schedule(self.bt_h, positions)
-        self.tok.copy_(torch.as_tensor(np.asarray(tokens, dtype=np.int32)))
-        self.slots.copy_(torch.from_numpy(slots))
-        self.lens.copy_(torch.from_numpy(lens_h))
+        self._upload.put([np.asarray(tokens), slots, lens_h])  # same sizes: same buffers
         self.graph.replay()
         return self.logits, self.tokens
 
