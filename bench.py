@@ -16,7 +16,9 @@ rotate over 4 buffer sets (> 512 MB) so the 256 MB last-level cache does not
 serve them warm.  ``value`` = algorithmic HBM bytes of the step / step time.
 
 Printed: ONE JSON line with the metric, a per-kernel breakdown (HBM GB/s or MFMA
-TFLOP/s against the chip's peak; for the two projections also the vendor GEMM,
+TFLOP/s against the chip's peak, from hipEvents around each call of the timed
+steps, and again from graph-replayed calls over the same rotating buffer sets,
+which leaves out the events' own cost; for the two projections also the vendor GEMM,
 hipBLASLt through torch.matmul, timed interleaved on the same operands as
 context), the ``roofline`` object of the dominant kernel
 (decode attention), the shape-tuned twins' times and the determinism slowdown
@@ -594,6 +596,24 @@ def main():
         kernels[n] = k
     step_bytes = sum(w["bytes"] for w in work.values())
     value = step_bytes / (ms_step / 1e3) / 1e9
+
+    # the same calls' device time without the per-call events: each kernel's calls
+    # over the rotating buffer sets, 20 of them replayed as one HIP graph
+    for idx, n in enumerate(names):
+        fns = [wl.calls(i)[idx][1] for i in range(SETS)]
+
+        def rotate(fns=fns, it=iter(range(1 << 30))):
+            fns[next(it) % SETS]()
+        us = graph_time_fn(rotate) * 1e3
+        w = work[n]
+        k = kernels[n]
+        k["graph_us"] = round(us, 2)
+        if w["bound"] == "mfma":
+            k["graph_TFLOP/s"] = round(w["flops"] / us / 1e6, 1)
+            k["graph_frac_mfma_peak"] = round(w["flops"] / us / 1e6 / MFMA_BF16_PEAK_TFS, 4)
+        else:
+            k["graph_GB/s"] = round(w["bytes"] / us / 1e3, 1)
+            k["graph_frac_hbm_peak"] = round(w["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4)
 
     dom = kernels["decode_attn_bi"]
     roofline = {"bound": "hbm", "kernel": "decode_attn_bi (split + ordered merge)",
