@@ -88,6 +88,50 @@ def test_bf16_parity(rows, H):
         assert torch.isnan(out[:, H:].float()).all()
 
 
+@pytest.mark.parametrize("dtype,H", [(torch.bfloat16, 13), (torch.bfloat16, 1000),
+                                     (torch.bfloat16, 4096), (torch.float32, 13),
+                                     (torch.float32, 1000), (torch.float32, 2048),
+                                     (torch.float32, 3000)])
+def test_rows_bitwise_across_workgroup_shapes(dtype, H):
+    # the batch size picks eight waves per row (<= 256 rows), four (< 2048) or one
+    # (>= 2048, and for rows longer than 512 chunks); every row must keep its bits
+    # through each switch, ragged row ends and both dtypes included
+    vec = 8 if dtype == torch.bfloat16 else 4
+    xs = vec * ((H + vec - 1) // vec)
+    rows = 2100
+    x = synth.normal((rows, H), seed=H + 11, dtype=torch.float32)
+    w = synth.normal((H,), std=0.1, mean=1.0, seed=synth.SEED_WEIGHTS, dtype=torch.float32)
+    xg = torch.zeros((rows, xs), dtype=dtype, device=DEV)
+    xg[:, :H] = x.to(DEV).to(dtype)
+    wg = torch.zeros(xs, dtype=dtype, device=DEV)
+    wg[:H] = w.to(DEV).to(dtype)
+    code = 1 if dtype == torch.bfloat16 else 0
+
+    def run(n):
+        out = torch.full((n, xs), float("nan"), dtype=dtype, device=DEV)
+        st = rbi.lib().rmsnorm_bi(xg.data_ptr(), xs, wg.data_ptr(), out.data_ptr(), xs, n, H,
+                                  EPS, code, torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        return out
+
+    full = run(rows)
+    for n in (1, 37, 256, 257, 300, 2047):
+        assert torch.equal(run(n)[:, :H], full[:n, :H]), n
+    if xs > H:
+        assert torch.isnan(full[:, H:].float()).all()
+    # parity of sampled rows against the oracle
+    pick = [0, 1, 255, 256, 2046, 2099]
+    if dtype == torch.bfloat16:
+        xb, wb = synth.bf16_bits(xg[pick, :H].cpu()), synth.bf16_bits(wg[:H].cpu())
+        ref = oracle.rmsnorm(xb, wb, EPS)
+        ok = _bf16_bracket_ok(synth.bf16_bits(full[pick, :H].cpu().contiguous()), ref)
+        assert ok.all()
+    else:
+        ref = oracle.rmsnorm(xg[pick, :H].cpu().numpy(), wg[:H].cpu().numpy(), EPS)
+        y = full[pick, :H].cpu().double().numpy()
+        assert (np.abs(y - ref) <= 1e-5 * np.abs(ref)).all()
+
+
 def test_bf16_rows_bitwise_over_every_batch_size():
     # hidden 4096, x ~ N(0,1) with 1% of rows x100; probes: an ordinary row, a scaled
     # row and the absorption row; every batch size 1..8192, probe at the first, last
