@@ -40,7 +40,11 @@ def test_c1_parity_and_rows_bitwise_across_batch():
 
 @pytest.mark.parametrize("M,N,K", [(1, 512, 256), (17, 4096, 4096), (130, 260, 1032),
                                    (257, 9216, 512), (64, 128, 8), (300, 260, 576),
-                                   (600, 1004, 128)])
+                                   (600, 1004, 128),
+                                   # the register-streaming tile (M <= 16, <= 256 tiles of 16
+                                   # columns): ragged N, a single k step, a step count that
+                                   # is not a multiple of its ring, M at its limit
+                                   (5, 20, 32), (3, 36, 4000), (16, 4096, 352)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_integer_inputs_exact(M, N, K, out_dtype):
     # integers in [-4, 4]: every partial sum is an integer below 2^24, so fp32 is exact
