@@ -309,6 +309,13 @@ __device__ __forceinline__ void combine_acc(const float (*c_acc)[16][D + CPAD],
     }
 }
 
+// The value v holds in lane `src` (the same src in every lane), read into a scalar
+// register: exact, and without the LDS round trip of a general lane permute.
+__device__ __forceinline__ float lane_value(float v, int src)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
 // Ascending fold of split partials (the merge): with M the largest partial
 // maximum folded so far (-inf before the first), a new partial (m, l_s, a_s)
 // gives M' = max(M, m), al = 2^(M - M'), be = 2^(m - M'),
@@ -478,7 +485,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
             Mp = M;
         const float al_l = exp2_hw(Mp - Mi);
         const float be_l = exp2_hw(m_l - Mi);
-        M = __shfl(Mi, 63, kWave);
+        M = lane_value(Mi, 63);
         const int cnt = min(64, n - s0);
         for (int j0 = 0; j0 < cnt; j0 += UNROLL) {
             // every load issued before the first use; past the row's last split a
@@ -499,9 +506,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 if (j0 + u < cnt) {
-                    const float al = __shfl(al_l, j0 + u, kWave);
-                    const float be = __shfl(be_l, j0 + u, kWave);
-                    l = fold_step(l, al, be, __shfl(l_l, j0 + u, kWave));
+                    // split j0 + u's factors from its lane: the lane index is the same in
+                    // every lane, so a scalar read (v_readlane) rather than an LDS permute
+                    const float al = lane_value(al_l, j0 + u);
+                    const float be = lane_value(be_l, j0 + u);
+                    l = fold_step(l, al, be, lane_value(l_l, j0 + u));
 #pragma unroll
                     for (int e = 0; e < EPL; ++e)
                         o[e] = fold_step(o[e], al, be, a[u][e]);
