@@ -579,10 +579,11 @@ struct TileCand {
 };
 constexpr TileCand kTiles[] = {{256, 256, 0.56}, {256, 128, 0.42}, {128, 128, 0.39},
                                {128, 64, 0.20},  {64, 64, 0.15},   {64, 32, 0.10},
-                               {16, 16, 0.0},    {32, 16, 0.0},    {16, 16, 0.0}};
-constexpr int kNumTiles = 6;  // priced by the cost model; the last three are one-wave
-                              // weight-streaming tiles for small M (rule below): 16 x 16
-                              // and 32 x 16 through LDS, and 16 x 16 in registers
+                               {16, 16, 0.0},    {32, 16, 0.0},    {16, 16, 0.0},
+                               {32, 32, 0.0}};
+constexpr int kNumTiles = 6;  // priced by the cost model; the rest are weight-streaming
+                              // tiles for small M (rule below): 16 x 16 and 32 x 16
+                              // through LDS, 16 x 16 in registers, two-wave 32 x 32
 
 // (rounds of 256 workgroups) x (tile area) / (throughput per unit area)
 double tile_cost(int i, int64_t M, int64_t N)
@@ -601,6 +602,10 @@ int best_tile(int64_t M, int64_t N, double *cost)
     //    trip and barrier of every step, is faster up to M = 16 (o_proj M = 1:
     //    20.6 -> 14.0 us, down projection 28.4 -> 18.7 us); with more tiles per
     //    unit the LDS kernels are as fast or faster (QKV M = 1: 16.9 vs 18.7 us);
+    //  * from M = 33 with N <= 4096, two-wave 32 x 32 tiles (o_proj M = 48:
+    //    31.2 -> 23.7 us, down projection M = 48: 52.2 -> 35.2 us; M = 64: 28.6 ->
+    //    24.7 and 49.2 -> 39.8 us): twice the workgroups of the 64-row tiles, more
+    //    rows per wave than 16 x 16;
     //  * otherwise 16 x 16 through LDS while there are at most 1024 of them, and
     //    for vocabulary-sized N up to M = 8 (lm_head M = 1: 217.9 -> 204.8 us);
     //  * else 32 x 16 up to M = 32.
@@ -609,6 +614,10 @@ int best_tile(int64_t M, int64_t N, double *cost)
         if (M <= 16 && t16 <= 256) {
             *cost = 0;
             return 8;
+        }
+        if (M > 32 && N <= 4096) {
+            *cost = 0;
+            return 9;
         }
         if (t16 <= 1024 || (M <= 8 && t16 > 2048)) {
             *cost = 0;
@@ -644,7 +653,8 @@ hipError_t launch_tile_shape(int i, const MatmulArgs &a, hipStream_t s, int spli
     case 5: return launch_pipe<64, 32, 2, 1, 16>(a, s, splits, k_split, c_split_stride);
     case 6: return launch_pipe<16, 16, 1, 1, 16>(a, s, splits, k_split, c_split_stride);
     case 7: return launch_pipe<32, 16, 1, 1, 16>(a, s, splits, k_split, c_split_stride);
-    default: return launch_stream<16, 12>(a, s, splits, k_split, c_split_stride);
+    case 8: return launch_stream<16, 12>(a, s, splits, k_split, c_split_stride);
+    default: return launch_pipe<32, 32, 2, 1, 16>(a, s, splits, k_split, c_split_stride);
     }
 }
 
