@@ -44,7 +44,10 @@ def test_c1_parity_and_rows_bitwise_across_batch():
                                    # the register-streaming tile (M <= 16, <= 256 tiles of 16
                                    # columns): ragged N, a single k step, a step count that
                                    # is not a multiple of its ring, M at its limit
-                                   (5, 20, 32), (3, 36, 4000), (16, 4096, 352)])
+                                   (5, 20, 32), (3, 36, 4000), (16, 4096, 352),
+                                   # the two-wave 32 x 32 tile (33 <= M <= 64, N <= 4096):
+                                   # ragged M and N
+                                   (40, 100, 320), (64, 4096, 1024)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_integer_inputs_exact(M, N, K, out_dtype):
     # integers in [-4, 4]: every partial sum is an integer below 2^24, so fp32 is exact
