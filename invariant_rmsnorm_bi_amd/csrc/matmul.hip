@@ -647,8 +647,12 @@ hipError_t launch_tile_shape(int i, const MatmulArgs &a, hipStream_t s, int spli
     switch (i) {
     case 0: return launch_pipe<256, 256, 2, 4, 4>(a, s, splits, k_split, c_split_stride);
     case 1: return launch_pipe<256, 128, 2, 2, 6>(a, s, splits, k_split, c_split_stride);
-    case 2: return launch_pipe<128, 128, 2, 2, 8>(a, s, splits, k_split, c_split_stride);
-    case 3: return launch_pipe<128, 64, 2, 2, 12>(a, s, splits, k_split, c_split_stride);
+    // 128-row tiles with four stages: 64 or 48 KiB of LDS, two or three workgroups per
+    // compute unit (measured as fast or faster than 8 and 12 stages at every M from
+    // 48 to 4096 on the decode-layer shapes, e.g. QKV M = 4096 as one 128 x 128 launch
+    // 427 -> 358 us)
+    case 2: return launch_pipe<128, 128, 2, 2, 4>(a, s, splits, k_split, c_split_stride);
+    case 3: return launch_pipe<128, 64, 2, 2, 4>(a, s, splits, k_split, c_split_stride);
     case 4: return launch_pipe<64, 64, 2, 2, 8>(a, s, splits, k_split, c_split_stride);
     case 5: return launch_pipe<64, 32, 2, 1, 16>(a, s, splits, k_split, c_split_stride);
     case 6: return launch_pipe<16, 16, 1, 1, 16>(a, s, splits, k_split, c_split_stride);
