@@ -468,8 +468,28 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
         o[e] = 0.f;
     for (int s0 = 0; s0 < n; s0 += 64) {
         const int sl = s0 + lane;
-        // unconditional loads (a lane past the last split re-reads it), selected after
+        const int cnt = min(64, n - s0);
+        // every load issued before its first use; past the row's last split a lane
+        // re-reads that split (its value is never folded)
+        float a[UNROLL][EPL];
+        auto load_batch = [&](int j0) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const float *src = ac + (int64_t)(s0 + min(j0 + u, cnt - 1)) * D;
+                if constexpr (EPL == 2) {
+                    const float2 t = *reinterpret_cast<const float2 *>(src);
+                    a[u][0] = t.x;
+                    a[u][1] = t.y;
+                } else {
+                    a[u][0] = src[0];
+                }
+            }
+        };
+        // the group's (m, l), and with them its first batch of partials, so that the
+        // scan below runs while they arrive (batch 1: 10.0 -> 8.9 us, same bits)
         const float2 ml_l = *reinterpret_cast<const float2 *>(ml + 2 * min(sl, n - 1));
+        load_batch(0);
+        asm volatile("" ::: "memory");
         const float m_l = sl < n ? ml_l.x : -INFINITY;
         const float l_l = sl < n ? ml_l.y : 0.f;
         float Mi = m_l;  // max(M, m_s0 .. m_sl)
@@ -486,23 +506,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
         const float al_l = exp2_hw(Mp - Mi);
         const float be_l = exp2_hw(m_l - Mi);
         M = lane_value(Mi, 63);
-        const int cnt = min(64, n - s0);
         for (int j0 = 0; j0 < cnt; j0 += UNROLL) {
-            // every load issued before the first use; past the row's last split a
-            // lane re-reads that split (its value is never folded)
-            float a[UNROLL][EPL];
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const float *src = ac + (int64_t)(s0 + min(j0 + u, cnt - 1)) * D;
-                if constexpr (EPL == 2) {
-                    const float2 t = *reinterpret_cast<const float2 *>(src);
-                    a[u][0] = t.x;
-                    a[u][1] = t.y;
-                } else {
-                    a[u][0] = src[0];
-                }
+            if (j0 > 0) {
+                load_batch(j0);
+                asm volatile("" ::: "memory");  // keep the batch ahead of its folds
             }
-            asm volatile("" ::: "memory");  // keep the batch of loads ahead of the folds
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 if (j0 + u < cnt) {
