@@ -121,11 +121,7 @@ __device__ __forceinline__ void unpack_chunk(const uint4 &q, float *v)
     }
 }
 
-// A full chunk of y = round((x * rsq) * w), with w already loaded.  The store is
-// non-temporal: y is written once and not read back by this kernel, and streaming it
-// out keeps back-to-back calls from meeting the previous call's output still being
-// written back (8192 x 4096 bf16 rows over rotating buffers: 28.1 -> 25.6 us a call).
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+// A full chunk of y = round((x * rsq) * w), with w already loaded.
 template <bool BF16>
 __device__ __forceinline__ void store_full_chunk(char *row, int64_t c, const float *v,
                                                  const float *w, float rsq)
@@ -147,8 +143,7 @@ __device__ __forceinline__ void store_full_chunk(char *row, int64_t c, const flo
         q.z = __float_as_uint(o[2]);
         q.w = __float_as_uint(o[3]);
     }
-    __builtin_nontemporal_store(u32x4_t{q.x, q.y, q.z, q.w},
-                                reinterpret_cast<u32x4_t *>(row + c * 16));
+    *reinterpret_cast<uint4 *>(row + c * 16) = q;
 }
 
 // Fixed pairwise tree over the per-slot partials of one lane.
