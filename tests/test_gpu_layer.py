@@ -311,3 +311,36 @@ def test_seeded_sampling_reproducible_in_any_batch(weights):
         p_tok = nxt[at]
         got.append(p_tok)
     assert got == ref
+
+
+def test_unsynchronised_steps_equal_synchronised(weights):
+    # a step's inputs reach the device through one pinned staging buffer (reused, and
+    # regrown when the batch grows) by an asynchronous copy; steps issued back to back
+    # with no host synchronisation must give the bits of the same steps run one at a
+    # time with a synchronisation after each
+    rng = np.random.default_rng(17)
+    rows_max, pages_per = 16, 8
+    table = np.zeros((rows_max, MAXP), dtype=np.int32)
+    for r in range(rows_max):
+        table[r, :pages_per] = np.arange(r * pages_per, (r + 1) * pages_per)
+    plan = []
+    for B in (1, 7, 3, 16, 2, 16, 5, 1, 12, 16):
+        rows = rng.choice(rows_max, size=B, replace=False)
+        plan.append((rng.integers(0, CFG.vocab, size=B), table[rows],
+                     rng.integers(0, pages_per * CFG.page_size, size=B)))
+
+    def run(sync):
+        layer = DecodeLayer(CFG, weights, num_pages=rows_max * pages_per, device=DEV)
+        outs = []
+        for toks, bt, pos in plan:
+            lg, tk = layer.step(toks, bt, pos)
+            outs.append((lg.clone(), tk.clone()))
+            if sync:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return outs
+
+    ref = run(True)
+    got = run(False)
+    for (lr, tr), (lg, tg) in zip(ref, got):
+        assert torch.equal(lr, lg) and torch.equal(tr, tg)
