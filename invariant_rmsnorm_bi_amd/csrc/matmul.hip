@@ -637,6 +637,21 @@ int best_tile(int64_t M, int64_t N, double *cost)
             bc = c;
         }
     }
+    // With N <= 4096 (the long-K o_proj and down projection shapes), a single
+    // partial round of 256 x 128 tiles is slower than the four-stage 128 x 128 tile
+    // at up to two workgroups per compute unit, which the per-round pricing above
+    // does not see (graph-replayed over four operand sets, o_proj M = 1280 / 1536:
+    // 144.9 / 146.0 -> 128.4 / 123.9 us; down projection: 226.8 / 226.6 -> 201.6 /
+    // 194.0 us).  With a full round (M = 2048) or a wide N (QKV, gate/up, where the
+    // 256 x 128 tile stays ahead) the priced choice stands.
+    if (best == 1 && N <= 4096) {
+        const int64_t t1 = ((M + 255) / 256) * ((N + 127) / 128);
+        const int64_t t2 = ((M + 127) / 128) * ((N + 127) / 128);
+        if (t1 < 256 && t2 <= 512) {
+            *cost = tile_cost(2, M, N);
+            return 2;
+        }
+    }
     *cost = bc;
     return best;
 }
