@@ -162,11 +162,11 @@ __device__ __forceinline__ float inv_rms(float sumsq, int64_t H, float eps)
     return 1.0f / sqrtf(ms + eps);
 }
 
-// One wavefront per row, RPW rows per workgroup (one row per workgroup for small
-// batches, so that even 256 rows reach 256 compute units).  Rows of up to 64*CPL
-// chunks stay in registers between the two passes; longer rows are read twice.
-// Both paths execute the same arithmetic in the same order.
-template <bool BF16, int CPL, int RPW>
+// One wavefront per row, RPW rows per workgroup, for rows too long to hold in
+// registers (more than 64 * 8 chunks): the row is read twice, once for the sum of
+// squares and once for the store.  This is the reference form of the reduction
+// order above; rmsnorm_split_kernel reproduces it for shorter rows.
+template <bool BF16, int RPW>
 __global__ __launch_bounds__(64 * RPW) void rmsnorm_wave_kernel(const char *x, int64_t xs,
                                                                 const char *__restrict__ w,
                                                                 char *y, int64_t ys,
@@ -186,79 +186,25 @@ __global__ __launch_bounds__(64 * RPW) void rmsnorm_wave_kernel(const char *x, i
 #pragma unroll
     for (int e = 0; e < VEC; ++e)
         part[e] = 0.f;
-
-    if (nchunks <= 64 * CPL) {
-        // Every full chunk's x and w are requested up front with unconditional
-        // 16-byte loads (a lane past the last full chunk re-reads that chunk and
-        // discards it), so a row costs one memory latency, not one per chunk; the
-        // partial chunk at the end of a row whose length is not a multiple of VEC
-        // is read element by element.
-        const int64_t nfull = H / VEC;
-        const bool tail = nfull < nchunks;
-        const char *wr = w;
-        uint4 xq[CPL], wq[CPL];
-        if (nfull > 0) {
+    for (int64_t c = lane; c < nchunks; c += 64) {
+        float v[VEC];
+        load_chunk<BF16>(xr, c, H, v);
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int64_t c = min((int64_t)lane + 64 * i, nfull - 1);
-                xq[i] = *reinterpret_cast<const uint4 *>(xr + c * 16);
-            }
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int64_t c = min((int64_t)lane + 64 * i, nfull - 1);
-                wq[i] = *reinterpret_cast<const uint4 *>(wr + c * 16);
-            }
-        }
-        float v[CPL][VEC];
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int64_t c = lane + 64 * i;
-            float t[VEC];
-            unpack_chunk<BF16>(xq[i], t);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                v[i][e] = c < nfull ? t[e] : 0.f;
-            if (tail && c == nfull)
-                load_chunk<BF16>(xr, c, H, v[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < CPL; ++i)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                part[e] = fmaf(v[i][e], v[i][e], part[e]);
-        const float rsq = inv_rms(wave_sum_butterfly(slot_tree<VEC>(part)), H, eps);
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int64_t c = lane + 64 * i;
-            if (c < nfull) {
-                float wv[VEC];
-                unpack_chunk<BF16>(wq[i], wv);
-                store_full_chunk<BF16>(yr, c, v[i], wv, rsq);
-            } else if (tail && c == nfull) {
-                store_chunk<BF16>(yr, w, c, H, v[i], rsq);
-            }
-        }
-    } else {
-        for (int64_t c = lane; c < nchunks; c += 64) {
-            float v[VEC];
-            load_chunk<BF16>(xr, c, H, v);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                part[e] = fmaf(v[e], v[e], part[e]);
-        }
-        const float rsq = inv_rms(wave_sum_butterfly(slot_tree<VEC>(part)), H, eps);
-        for (int64_t c = lane; c < nchunks; c += 64) {
-            float v[VEC];
-            load_chunk<BF16>(xr, c, H, v);
-            store_chunk<BF16>(yr, w, c, H, v, rsq);
-        }
+        for (int e = 0; e < VEC; ++e)
+            part[e] = fmaf(v[e], v[e], part[e]);
+    }
+    const float rsq = inv_rms(wave_sum_butterfly(slot_tree<VEC>(part)), H, eps);
+    for (int64_t c = lane; c < nchunks; c += 64) {
+        float v[VEC];
+        load_chunk<BF16>(xr, c, H, v);
+        store_chunk<BF16>(yr, w, c, H, v, rsq);
     }
 }
 
 // The wave-per-row arithmetic with the row's memory traffic spread over NWV waves,
-// for small batches (one row per workgroup): a single wave issues every load and
-// store of its row in sequence, which leaves a mostly idle chip waiting on one
-// wave per row.  Here wave v loads and stores the chunks of steps i = v*CPL/NWV ..
+// one row per workgroup, for rows of at most 64 * CPL chunks: a single wave issuing
+// every load and store of its row was slower at every batch size measured.  Here
+// wave v loads and stores the chunks of steps i = v*CPL/NWV ..
 // of every lane (lane l, step i: chunk l + 64 i, as in rmsnorm_wave_kernel), parks
 // their fp32 values in LDS, and after one barrier every wave reduces the whole row
 // exactly as the single wave does: lane l's slot partials over its chunks in
@@ -427,28 +373,30 @@ hipError_t launch_rmsnorm_wave(const void *x, int64_t xs, const void *w, void *y
                                hipStream_t s)
 {
     // The workgroup shape changes with the batch, never a row's arithmetic.
-    // Measured on MI355X with H = 4096 bf16 (device time of graph-replayed calls):
-    // up to 256 rows, eight waves per row (3.0-3.6 us; one wave per row 5.2-5.7 us);
-    // up to 2047 rows, four (1024 rows: 6.0 vs 7.1 us); from 2048 rows on, one wave
-    // per row and four rows per workgroup.  Rows longer than 64 * 8 chunks always
-    // take the wave kernel's two-pass path.
+    // Measured on MI355X with H = 4096 bf16 (device time of graph-replayed calls
+    // over four input sets): up to 256 rows, eight waves per row (3.0-3.6 us; one
+    // wave per row 5.2-5.7 us); beyond, four waves per row (2048 rows: 9.35 vs
+    // 9.84 us with one wave per row and four rows per workgroup, 6144: 22.3 vs
+    // 24.7 us, 8192: 27.0 vs 28.6 us; within 4 % of it at 3072-4096 rows).  Rows
+    // longer than 64 * 8 chunks take the two-pass wave kernel, four rows per
+    // workgroup from 4096 rows on.
     const int64_t vec = bf16 ? 8 : 4;
     const bool in_regs = (hidden + vec - 1) / vec <= 64 * 8;
-    if (rows >= 2048 || (!in_regs && rows >= 4096)) {
+    if (!in_regs && rows >= 4096) {
         const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
         if (bf16)
-            rmsnorm_wave_kernel<true, 8, 4><<<grid, block, 0, s>>>(
+            rmsnorm_wave_kernel<true, 4><<<grid, block, 0, s>>>(
                 (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
         else
-            rmsnorm_wave_kernel<false, 8, 4><<<grid, block, 0, s>>>(
+            rmsnorm_wave_kernel<false, 4><<<grid, block, 0, s>>>(
                 (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
     } else if (!in_regs) {
         const dim3 grid((unsigned)rows), block(64);
         if (bf16)
-            rmsnorm_wave_kernel<true, 8, 1><<<grid, block, 0, s>>>(
+            rmsnorm_wave_kernel<true, 1><<<grid, block, 0, s>>>(
                 (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
         else
-            rmsnorm_wave_kernel<false, 8, 1><<<grid, block, 0, s>>>(
+            rmsnorm_wave_kernel<false, 1><<<grid, block, 0, s>>>(
                 (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
     } else if (rows <= 256) {
         const dim3 grid((unsigned)rows), block(512);

@@ -93,12 +93,13 @@ def test_bf16_parity(rows, H):
                                      (torch.float32, 1000), (torch.float32, 2048),
                                      (torch.float32, 3000)])
 def test_rows_bitwise_across_workgroup_shapes(dtype, H):
-    # the batch size picks eight waves per row (<= 256 rows), four (< 2048) or one
-    # (>= 2048, and for rows longer than 512 chunks); every row must keep its bits
-    # through each switch, ragged row ends and both dtypes included
+    # the batch size picks eight waves per row (<= 256 rows) or four; rows longer
+    # than 512 chunks (fp32, H = 3000) take one wave per row, one row per workgroup
+    # below 4096 rows and four from there; every row must keep its bits through
+    # each switch, ragged row ends and both dtypes included
     vec = 8 if dtype == torch.bfloat16 else 4
     xs = vec * ((H + vec - 1) // vec)
-    rows = 2100
+    rows = 4100
     x = synth.normal((rows, H), seed=H + 11, dtype=torch.float32)
     w = synth.normal((H,), std=0.1, mean=1.0, seed=synth.SEED_WEIGHTS, dtype=torch.float32)
     xg = torch.zeros((rows, xs), dtype=dtype, device=DEV)
@@ -115,12 +116,12 @@ def test_rows_bitwise_across_workgroup_shapes(dtype, H):
         return out
 
     full = run(rows)
-    for n in (1, 37, 256, 257, 300, 2047):
+    for n in (1, 37, 256, 257, 300, 2047, 2048, 4095):
         assert torch.equal(run(n)[:, :H], full[:n, :H]), n
     if xs > H:
         assert torch.isnan(full[:, H:].float()).all()
     # parity of sampled rows against the oracle
-    pick = [0, 1, 255, 256, 2046, 2099]
+    pick = [0, 1, 255, 256, 2046, 4094, 4099]
     if dtype == torch.bfloat16:
         xb, wb = synth.bf16_bits(xg[pick, :H].cpu()), synth.bf16_bits(wg[:H].cpu())
         ref = oracle.rmsnorm(xb, wb, EPS)
