@@ -402,8 +402,9 @@ def prefill_points():
 def sampling_points():
     """sample_gumbel over the decode layer's lm_head logits (fp32 [rows, 151936],
     N(0, 2) values, per-row seeds and positions, temperature 0.8) at 1 and 128
-    rows, against the greedy rbi_argmax_rows over the same logits: device time
-    (median of 20) and the logits' read rate."""
+    rows, against the greedy rbi_argmax_rows over the same logits: device time of
+    graph-replayed calls (the binding's host cost is not in it), the logits' read
+    rate, and the rate of calls queued from Python for comparison."""
     pts = []
     V = 151936
     for rows in (1, 128):
@@ -413,12 +414,16 @@ def sampling_points():
         temps = torch.full((rows,), 0.8, device=DEV)
         ws = torch.empty(rbi.sample_gumbel_workspace_size(rows, V), dtype=torch.uint8, device=DEV)
         tok = torch.empty(rows, dtype=torch.int32, device=DEV)
-        t_s = time_fn(lambda: rbi.sample_gumbel(x, seeds, pos, temps, out=tok, workspace=ws))
-        t_g = time_fn(lambda: rbi.argmax_rows(x))
+        tok_g = torch.empty(rows, dtype=torch.int32, device=DEV)
+        f_s = lambda: rbi.sample_gumbel(x, seeds, pos, temps, out=tok, workspace=ws)  # noqa: E731
+        f_g = lambda: rbi.argmax_rows(x, out=tok_g)  # noqa: E731
+        q_s, q_g = time_fn(f_s), time_fn(f_g)
+        t_s, t_g = graph_time_fn(f_s), graph_time_fn(f_g)
         nbytes = rows * V * 4
         pts.append({"point": f"sample_gumbel rows={rows} vocab={V}", "us": round(t_s * 1e3, 2),
                     "GB/s": round(nbytes / (t_s * 1e-3) / 1e9, 1),
-                    "greedy_argmax_us": round(t_g * 1e3, 2)})
+                    "greedy_argmax_us": round(t_g * 1e3, 2),
+                    "queued_us": round(q_s * 1e3, 2), "greedy_queued_us": round(q_g * 1e3, 2)})
         del x, ws
     return pts
 
