@@ -557,8 +557,11 @@ def main():
                     help="also run a plain 1 GiB copy (counter calibration for profiles/)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(kernels are per-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path. The kernels "
+              "work on one GPU's share (rows for RMSNorm, weight columns or K ranges for the "
+              "matmul, KV heads or splits for attention), so a sharded deployment runs "
+              "them per GPU.",
+              file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
     rbi.lib()
