@@ -206,10 +206,12 @@ __global__ __launch_bounds__(64 * RPW) void rmsnorm_wave_kernel(const char *x, i
 // every load and store of its row was slower at every batch size measured.  Here
 // wave v loads and stores the chunks of steps i = v*CPL/NWV ..
 // of every lane (lane l, step i: chunk l + 64 i, as in rmsnorm_wave_kernel), parks
-// their fp32 values in LDS, and after one barrier every wave reduces the whole row
+// their fp32 values in LDS, and after one barrier wave 0 reduces the whole row
 // exactly as the single wave does: lane l's slot partials over its chunks in
-// ascending step order, the slot tree and the butterfly.  Each wave then writes its
-// own chunks with that rsq.  Rows of at most 64 * CPL chunks.
+// ascending step order, the slot tree and the butterfly.  After a second barrier
+// every wave writes its own chunks with that rsq (letting every wave repeat the
+// reduction instead read the row from LDS NWV times and was 6-14 % slower).
+// Rows of at most 64 * CPL chunks.
 template <bool BF16, int CPL, int NWV>
 __global__ __launch_bounds__(64 * NWV) void rmsnorm_split_kernel(const char *x, int64_t xs,
                                                                  const char *__restrict__ w,
@@ -262,18 +264,26 @@ __global__ __launch_bounds__(64 * NWV) void rmsnorm_split_kernel(const char *x, 
     }
     __syncthreads();
 
-    float part[VEC];
+    // wave 0 reduces the row; the other waves take its rsq from LDS
+    __shared__ float rsq_lds;
+    if (wv == 0) {
+        float part[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e)
-        part[e] = 0.f;
+        for (int e = 0; e < VEC; ++e)
+            part[e] = 0.f;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i)
+        for (int i = 0; i < CPL; ++i)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const float a = vs[i * VEC + e][lane];
-            part[e] = fmaf(a, a, part[e]);
-        }
-    const float rsq = inv_rms(wave_sum_butterfly(slot_tree<VEC>(part)), H, eps);
+            for (int e = 0; e < VEC; ++e) {
+                const float a = vs[i * VEC + e][lane];
+                part[e] = fmaf(a, a, part[e]);
+            }
+        const float r = inv_rms(wave_sum_butterfly(slot_tree<VEC>(part)), H, eps);
+        if (lane == 0)
+            rsq_lds = r;
+    }
+    __syncthreads();
+    const float rsq = rsq_lds;
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
         const int64_t c = lane + 64 * (wv * SPW + j);
@@ -374,12 +384,12 @@ hipError_t launch_rmsnorm_wave(const void *x, int64_t xs, const void *w, void *y
 {
     // The workgroup shape changes with the batch, never a row's arithmetic.
     // Measured on MI355X with H = 4096 bf16 (device time of graph-replayed calls
-    // over four input sets): up to 256 rows, eight waves per row (3.0-3.6 us; one
-    // wave per row 5.2-5.7 us); beyond, four waves per row (2048 rows: 9.35 vs
-    // 9.84 us with one wave per row and four rows per workgroup, 6144: 22.3 vs
-    // 24.7 us, 8192: 27.0 vs 28.6 us; within 4 % of it at 3072-4096 rows).  Rows
-    // longer than 64 * 8 chunks take the two-pass wave kernel, four rows per
-    // workgroup from 4096 rows on.
+    // over four input sets): up to 1024 rows, eight waves per row (1 row 2.8 us,
+    // 512 rows 4.0 us, 1024 rows 5.9 us; four waves 3.3, 4.3, 6.1 us); beyond,
+    // four waves per row (1536 rows 7.5 vs 8.2 us with eight, 4096 rows 13.3 vs
+    // 14.8, 8192 rows 26.2 vs 28.9; one wave per row, four rows per workgroup:
+    // 28.6 us at 8192 rows).  Rows longer than 64 * 8 chunks take the two-pass
+    // wave kernel, four rows per workgroup from 4096 rows on.
     const int64_t vec = bf16 ? 8 : 4;
     const bool in_regs = (hidden + vec - 1) / vec <= 64 * 8;
     if (!in_regs && rows >= 4096) {
@@ -398,7 +408,7 @@ hipError_t launch_rmsnorm_wave(const void *x, int64_t xs, const void *w, void *y
         else
             rmsnorm_wave_kernel<false, 1><<<grid, block, 0, s>>>(
                 (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
-    } else if (rows <= 256) {
+    } else if (rows <= 1024) {
         const dim3 grid((unsigned)rows), block(512);
         if (bf16)
             rmsnorm_split_kernel<true, 8, 8><<<grid, block, 0, s>>>(

@@ -93,7 +93,7 @@ def test_bf16_parity(rows, H):
                                      (torch.float32, 1000), (torch.float32, 2048),
                                      (torch.float32, 3000)])
 def test_rows_bitwise_across_workgroup_shapes(dtype, H):
-    # the batch size picks eight waves per row (<= 256 rows) or four; rows longer
+    # the batch size picks eight waves per row (<= 1024 rows) or four; rows longer
     # than 512 chunks (fp32, H = 3000) take one wave per row, one row per workgroup
     # below 4096 rows and four from there; every row must keep its bits through
     # each switch, ragged row ends and both dtypes included
@@ -116,12 +116,12 @@ def test_rows_bitwise_across_workgroup_shapes(dtype, H):
         return out
 
     full = run(rows)
-    for n in (1, 37, 256, 257, 300, 2047, 2048, 4095):
+    for n in (1, 37, 256, 257, 1024, 1025, 2047, 2048, 4095):
         assert torch.equal(run(n)[:, :H], full[:n, :H]), n
     if xs > H:
         assert torch.isnan(full[:, H:].float()).all()
     # parity of sampled rows against the oracle
-    pick = [0, 1, 255, 256, 2046, 4094, 4099]
+    pick = [0, 1, 1023, 1024, 2046, 4094, 4099]
     if dtype == torch.bfloat16:
         xb, wb = synth.bf16_bits(xg[pick, :H].cpu()), synth.bf16_bits(wg[:H].cpu())
         ref = oracle.rmsnorm(xb, wb, EPS)
