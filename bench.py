@@ -33,7 +33,6 @@ import json
 import math
 import os
 import platform
-import subprocess
 import sys
 import time
 
@@ -521,11 +520,7 @@ def copy_probe():
 
 def fingerprint():
     p = torch.cuda.get_device_properties(0)
-    try:
-        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short", "HEAD"],
-                             capture_output=True, text=True).stdout.strip()
-    except Exception:
-        sha = ""
+    build = rbi.build_info()  # stamped into librbi.so when it was built
     cpu = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -536,7 +531,7 @@ def fingerprint():
     except OSError:
         pass
     return {"gpu": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
-            "torch": torch.__version__, "hip": torch.version.hip, "git": sha, "host_cpu": cpu,
+            "torch": torch.__version__, "hip": torch.version.hip, "build": build, "host_cpu": cpu,
             "host_threads": os.cpu_count(), "python": platform.python_version(),
             "seeds": {"data": synth.SEED_DATA, "weights": synth.SEED_WEIGHTS,
                       "batch": synth.SEED_BATCH, "pages": synth.SEED_PAGES}}

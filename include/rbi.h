@@ -61,6 +61,11 @@ const char *rbi_status_string(int status);
 /* Library ABI version, incremented on any signature change. */
 int rbi_abi_version(void);
 
+/* What the library was built from (static string, never NULL): "git=<commit>"
+ * (suffixed "-dirty" when the checkout had uncommitted changes) and
+ * "src_sha256=<first 16 hex digits>" over the kernel and ABI sources. */
+const char *rbi_build_info(void);
+
 /* -------------------------------------------------------------------------- */
 /* RMSNorm                                                                     */
 /* -------------------------------------------------------------------------- */
@@ -112,10 +117,25 @@ int rmsnorm_tuned(const void *x, int64_t x_row_stride, const void *w, void *y,
  *  C  [M, N] c_dtype, row stride ldc.
  * Requirements: A, W 16-byte aligned, lda and ldw multiples of 8, K a positive
  * multiple of 8, lda >= K, ldw >= K; C 16-byte aligned, ldc a multiple of 4,
- * ldc >= N, N a multiple of 4.  Otherwise RBI_EINVAL.
+ * ldc >= N, N a multiple of 4.  Otherwise RBI_EINVAL.  Sizes with
+ * ceil(M/16) * ceil(N/16) >= 2^26 (more threads than one launch holds) give
+ * RBI_EUNSUPPORTED.
  */
 int matmul_bi(const void *A, int64_t lda, const void *W, int64_t ldw, void *C, int64_t ldc,
               int c_dtype, int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * matmul_bi_plan: which launches matmul_bi makes for (M, N, K), for tests that
+ * must reach every tile shape and for tuning.  The choice only decides which
+ * wave computes an element, never the element's arithmetic.  Fills plan[7]
+ * (host memory): {tile rows, tile columns, kind} of the first launch, the
+ * number of columns it covers (N when there is one launch), then {tile rows,
+ * tile columns, kind} of the launch over the remaining columns (zeros when
+ * there is none).  kind: 0 LDS-pipelined tile, 1 register-streaming tile,
+ * 2 register-staged tile (K % 32 != 0).  Returns RBI_EINVAL for sizes matmul_bi
+ * would reject; needs no GPU.
+ */
+int matmul_bi_plan(int64_t M, int64_t N, int64_t K, int64_t *plan);
 
 /*
  * matmul_tuned: same function.  Chooses split-K from (M, N, K) so that small-M

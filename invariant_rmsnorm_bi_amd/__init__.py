@@ -24,8 +24,8 @@ import os
 import torch
 
 __all__ = [
-    "RbiError", "lib", "lib_path", "rmsnorm_bi", "rmsnorm_tuned", "matmul_bi", "matmul_tuned",
-    "matmul_tuned_workspace_size", "decode_attn_bi", "decode_attn_tuned",
+    "RbiError", "lib", "lib_path", "build_info", "rmsnorm_bi", "rmsnorm_tuned", "matmul_bi", "matmul_tuned",
+    "matmul_tuned_workspace_size", "matmul_bi_plan", "decode_attn_bi", "decode_attn_tuned",
     "decode_attn_workspace_size", "decode_attn_tuned_split_size", "prefill_attn_bi",
     "prefill_attn_workspace_size", "sample_gumbel", "sample_gumbel_workspace_size",
     "kv_append", "embed",
@@ -39,8 +39,8 @@ RBI_F32, RBI_BF16 = 0, 1
 
 # every symbol include/rbi.h declares
 EXPORTS = (
-    "rbi_status_string", "rbi_abi_version", "rmsnorm_bi", "rmsnorm_tuned", "matmul_bi",
-    "matmul_tuned", "matmul_tuned_workspace_size", "decode_attn_workspace_size",
+    "rbi_status_string", "rbi_abi_version", "rbi_build_info", "rmsnorm_bi", "rmsnorm_tuned", "matmul_bi",
+    "matmul_tuned", "matmul_tuned_workspace_size", "matmul_bi_plan", "decode_attn_workspace_size",
     "decode_attn_bi", "decode_attn_tuned_split_size", "decode_attn_tuned",
     "prefill_attn_workspace_size", "prefill_attn_bi", "sample_gumbel_workspace_size",
     "sample_gumbel", "kv_append",
@@ -74,10 +74,12 @@ def lib() -> ctypes.CDLL:
     sig = {
         "rbi_status_string": ([i32], ctypes.c_char_p),
         "rbi_abi_version": ([], i32),
+        "rbi_build_info": ([], ctypes.c_char_p),
         "rmsnorm_bi": ([p, i64, p, p, i64, i64, i64, f32, i32, p], i32),
         "rmsnorm_tuned": ([p, i64, p, p, i64, i64, i64, f32, i32, p], i32),
         "matmul_bi": ([p, i64, p, i64, p, i64, i32, i64, i64, i64, p], i32),
         "matmul_tuned_workspace_size": ([i64, i64, i64], sz),
+        "matmul_bi_plan": ([i64, i64, i64, p], i32),
         "matmul_tuned": ([p, i64, p, i64, p, i64, i32, i64, i64, i64, p, sz, p], i32),
         "decode_attn_workspace_size": ([i64, i32, i32, i32, i32], sz),
         "decode_attn_bi": ([p, i64, p, p, p, i64, p, p, i64, i64, i32, i32, i32, i32, i32, i32,
@@ -102,6 +104,11 @@ def lib() -> ctypes.CDLL:
         fn.restype = res
     _lib = L
     return L
+
+
+def build_info() -> str:
+    """The commit and source hash librbi.so was built from (rbi_build_info)."""
+    return lib().rbi_build_info().decode()
 
 
 def _check(status: int, what: str) -> None:
@@ -200,6 +207,16 @@ def matmul_bi(A: torch.Tensor, W: torch.Tensor, out_dtype=torch.bfloat16, out=No
                          _row_stride(out), _dtype_code(out), M, N, K, _stream())
     _check(st, "matmul_bi")
     return out
+
+
+def matmul_bi_plan(M: int, N: int, K: int) -> dict:
+    """The launches matmul_bi makes for (M, N, K): {"first": (rows, cols, kind),
+    "n1": columns of the first launch, "second": (rows, cols, kind) or None};
+    kind 0 LDS-pipelined, 1 register streaming, 2 register-staged.  Host only."""
+    buf = (ctypes.c_int64 * 7)()
+    _check(lib().matmul_bi_plan(M, N, K, buf), "matmul_bi_plan")
+    v = list(buf)
+    return {"first": tuple(v[0:3]), "n1": v[3], "second": tuple(v[4:7]) if v[4] else None}
 
 
 def matmul_tuned_workspace_size(M: int, N: int, K: int) -> int:

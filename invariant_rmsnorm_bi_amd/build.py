@@ -47,9 +47,30 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build librbi)")
 
 
-def _compile(src: str) -> str:
+def build_info() -> str:
+    """What the library is built from: the git commit of the tree (with "-dirty" when
+    tracked files differ from it, "none" outside a checkout) and a sha256 over the
+    sources that go into the library, so a result can be traced to its code."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(INCLUDE, "rbi.h")]:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    root = os.path.dirname(PKG)
+    try:
+        sha = subprocess.run(["git", "-C", root, "rev-parse", "--short=12", "HEAD"],
+                             capture_output=True, text=True, timeout=10).stdout.strip()
+        dirty = subprocess.run(["git", "-C", root, "status", "--porcelain", "--untracked-files=no"],
+                               capture_output=True, text=True, timeout=10).stdout.strip()
+        git = (sha + ("-dirty" if dirty else "")) if sha else "none"
+    except (OSError, subprocess.SubprocessError):
+        git = "none"
+    return f"git={git} src_sha256={h.hexdigest()[:16]}"
+
+
+def _compile(src: str, info: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, f'-DRBI_BUILD_INFO="{info}"', "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
@@ -59,8 +80,9 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    info = build_info()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda src: _compile(src, info), srcs))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

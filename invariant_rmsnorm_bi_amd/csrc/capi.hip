@@ -60,6 +60,10 @@ int check_matmul(const void *A, int64_t lda, const void *W, int64_t ldw, void *C
         return RBI_EINVAL;
     if (M > (int64_t)0x3fffffff || N > (int64_t)0x3fffffff || K > (int64_t)0x3fffffff)
         return RBI_EUNSUPPORTED;
+    // grid bound: the smallest tile is 16 x 16 on one 64-lane wave, and a launch
+    // holds fewer than 2^32 threads (the tile count is also kept in an int)
+    if (((M + 15) / 16) * ((N + 15) / 16) >= ((int64_t)1 << 26))
+        return RBI_EUNSUPPORTED;
     return RBI_OK;
 }
 
@@ -115,6 +119,15 @@ int rbi_abi_version(void)
     return 1;
 }
 
+#ifndef RBI_BUILD_INFO
+#define RBI_BUILD_INFO "git=unknown src_sha256=unknown"
+#endif
+
+const char *rbi_build_info(void)
+{
+    return RBI_BUILD_INFO;
+}
+
 int rmsnorm_bi(const void *x, int64_t x_row_stride, const void *w, void *y, int64_t y_row_stride,
                int64_t rows, int64_t hidden, float eps, int dtype, void *stream)
 {
@@ -150,6 +163,14 @@ int matmul_bi(const void *A, int64_t lda, const void *W, int64_t ldw, void *C, i
     const rbi::MatmulArgs a{(const uint16_t *)A, lda, (const uint16_t *)W, ldw, C, ldc,
                             c_dtype == RBI_BF16, M, N, K};
     return launched(rbi::launch_matmul_bi(a, stream_of(stream)));
+}
+
+int matmul_bi_plan(int64_t M, int64_t N, int64_t K, int64_t *plan)
+{
+    if (!plan || M < 1 || N < 1 || K < 8 || K % 8 || N % 4)
+        return RBI_EINVAL;
+    rbi::describe_matmul_plan(rbi::plan_matmul_bi(M, N, K), plan);
+    return RBI_OK;
 }
 
 size_t matmul_tuned_workspace_size(int64_t M, int64_t N, int64_t K)

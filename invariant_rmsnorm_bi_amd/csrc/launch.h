@@ -28,6 +28,17 @@ struct MatmulArgs {
     bool c_bf16;
     int64_t M, N, K;
 };
+// The launches matmul_bi makes for a problem size: tile shape t1 over the first n1
+// columns, then tile shape t2 over the rest (t2 < 0: one launch over all N); t1 < 0
+// is the register-staged 128 x 128 kernel for K % 32 != 0.  Shapes index the tile
+// table of matmul.hip.
+struct MatmulPlan {
+    int t1;
+    int64_t n1;
+    int t2;
+};
+MatmulPlan plan_matmul_bi(int64_t M, int64_t N, int64_t K);
+void describe_matmul_plan(const MatmulPlan &p, int64_t out[7]);
 hipError_t launch_matmul_bi(const MatmulArgs &a, hipStream_t s);
 // split-K twin: `splits` partial products over equal K ranges into fp32 workspace
 // [splits, M, N], then an ascending-order reduction into C.

@@ -677,7 +677,7 @@ hipError_t launch_tile_shape(int i, const MatmulArgs &a, hipStream_t s, int spli
     }
 }
 
-hipError_t launch_matmul_bi(const MatmulArgs &a, hipStream_t s)
+MatmulPlan plan_matmul_bi(int64_t M, int64_t N, int64_t K)
 {
     // The tile shape is picked from the problem size; that changes which wave
     // computes an element, never the element's arithmetic.  Big tiles are efficient
@@ -686,51 +686,77 @@ hipError_t launch_matmul_bi(const MatmulArgs &a, hipStream_t s)
     // last round of workgroups mostly empty, the columns are cut in two: the first
     // N1 columns in full rounds of a big tile, the rest with the shape that suits
     // them, as two launches on the same stream.
-    if (a.K % PK == 0) {
-        double c1;
-        const int t1 = best_tile(a.M, a.N, &c1);
-        if (t1 <= 1) {
-            // a partly filled last round of big tiles runs faster than a full one
-            // (less contention); price it at sqrt(fill) of a round for this choice
-            const TileCand &c = kTiles[t1];
-            const int64_t tiles = ((a.M + c.tbm - 1) / c.tbm) * ((a.N + c.tbn - 1) / c.tbn);
-            const int64_t full = tiles / 256, rem = tiles % 256;
-            c1 = ((double)full + (rem ? std::sqrt(rem / 256.0) : 0.0)) * c.tbm * c.tbn / c.eff;
-        }
-        int split_t = -1, split_r = -1;
-        int64_t split_n = 0;
-        double best = c1;
-        for (int i = 0; i < 2; ++i) {  // the big shapes as the first part
-            const int64_t tbn = kTiles[i].tbn;
-            for (int64_t n1 = (a.N / tbn) * tbn; n1 >= tbn && n1 * 2 >= a.N; n1 -= tbn) {
-                if (n1 == a.N)
-                    continue;
-                double c2;
-                const int r = best_tile(a.M, a.N - n1, &c2);
-                if (r >= kNumTiles)
-                    continue;  // small-M tiles are not priced; keep one launch
-                const double c = tile_cost(i, a.M, n1) + c2;
-                if (c < best * 0.95) {  // a clear win only: two launches cost a little
-                    best = c;
-                    split_t = i;
-                    split_r = r;
-                    split_n = n1;
-                }
+    MatmulPlan p{-1, N, -1};
+    if (K % PK != 0)
+        return p;  // the register-staged 128 x 128 tile kernel
+    double c1;
+    const int t1 = best_tile(M, N, &c1);
+    if (t1 <= 1) {
+        // a partly filled last round of big tiles runs faster than a full one
+        // (less contention); price it at sqrt(fill) of a round for this choice
+        const TileCand &c = kTiles[t1];
+        const int64_t tiles = ((M + c.tbm - 1) / c.tbm) * ((N + c.tbn - 1) / c.tbn);
+        const int64_t full = tiles / 256, rem = tiles % 256;
+        c1 = ((double)full + (rem ? std::sqrt(rem / 256.0) : 0.0)) * c.tbm * c.tbn / c.eff;
+    }
+    p.t1 = t1;
+    double best = c1;
+    for (int i = 0; i < 2; ++i) {  // the big shapes as the first part
+        const int64_t tbn = kTiles[i].tbn;
+        for (int64_t n1 = (N / tbn) * tbn; n1 >= tbn && n1 * 2 >= N; n1 -= tbn) {
+            if (n1 == N)
+                continue;
+            double c2;
+            const int r = best_tile(M, N - n1, &c2);
+            if (r >= kNumTiles)
+                continue;  // small-M tiles are not priced; keep one launch
+            const double c = tile_cost(i, M, n1) + c2;
+            if (c < best * 0.95) {  // a clear win only: two launches cost a little
+                best = c;
+                p = MatmulPlan{i, n1, r};
             }
         }
-        if (split_t < 0)
-            return launch_tile_shape(t1, a, s);
-        MatmulArgs left = a, right = a;
-        left.N = split_n;
-        right.N = a.N - split_n;
-        right.W = a.W + split_n * a.ldw;
-        right.C = a.c_bf16 ? (void *)((uint16_t *)a.C + split_n) : (void *)((float *)a.C + split_n);
-        hipError_t e = launch_tile_shape(split_t, left, s);
-        if (e != hipSuccess)
-            return e;
-        return launch_tile_shape(split_r, right, s);
     }
-    return launch_tiles(a, 1, a.K, a.C, a.ldc, a.c_bf16, 0, s);
+    return p;
+}
+
+void describe_matmul_plan(const MatmulPlan &p, int64_t out[7])
+{
+    // tile rows, tile columns and kind (0 LDS-pipelined, 1 register streaming,
+    // 2 register-staged for K % 32 != 0) of each launch, and the first launch's
+    // column count
+    auto put = [&](int t, int64_t *o) {
+        if (t < 0) {
+            o[0] = BM, o[1] = BN, o[2] = 2;
+        } else {
+            o[0] = kTiles[t].tbm, o[1] = kTiles[t].tbn, o[2] = t == 8 ? 1 : 0;
+        }
+    };
+    put(p.t1, out);
+    out[3] = p.n1;
+    if (p.t2 >= 0) {
+        put(p.t2, out + 4);
+    } else {
+        out[4] = out[5] = out[6] = 0;
+    }
+}
+
+hipError_t launch_matmul_bi(const MatmulArgs &a, hipStream_t s)
+{
+    const MatmulPlan p = plan_matmul_bi(a.M, a.N, a.K);
+    if (p.t1 < 0)
+        return launch_tiles(a, 1, a.K, a.C, a.ldc, a.c_bf16, 0, s);
+    if (p.t2 < 0)
+        return launch_tile_shape(p.t1, a, s);
+    MatmulArgs left = a, right = a;
+    left.N = p.n1;
+    right.N = a.N - p.n1;
+    right.W = a.W + p.n1 * a.ldw;
+    right.C = a.c_bf16 ? (void *)((uint16_t *)a.C + p.n1) : (void *)((float *)a.C + p.n1);
+    hipError_t e = launch_tile_shape(p.t1, left, s);
+    if (e != hipSuccess)
+        return e;
+    return launch_tile_shape(p.t2, right, s);
 }
 
 // Split count of the twin.  With K a multiple of 32 it takes the tile shape the

@@ -220,3 +220,32 @@ def test_sample_gumbel_validation():
     assert f(FAKE, 151936, -1, 151936, FAKE, FAKE, FAKE, FAKE, FAKE, need, NULL) == EINVAL
     assert f(FAKE, 151936, 4, 151936, FAKE, FAKE, FAKE, FAKE, NULL, need, NULL) == EWORKSPACE
     assert f(FAKE, 151936, 4, 151936, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, NULL) == EWORKSPACE
+
+
+def test_exact_matmul_cases_reach_every_tile_shape():
+    # the integer-exact GPU cases must run every tile shape matmul_bi can launch
+    # (the plan is a host-side choice, so this needs no GPU)
+    from tests.test_gpu_matmul import BIG_EXACT_CASES, SMALL_EXACT_CASES
+    seen = set()
+    for mnk in SMALL_EXACT_CASES + [c for c, _ in BIG_EXACT_CASES]:
+        p = rbi.matmul_bi_plan(*mnk)
+        seen.add(p["first"])
+        if p["second"]:
+            seen.add(p["second"])
+    every = {(256, 256, 0), (256, 128, 0), (128, 128, 0), (128, 64, 0), (64, 64, 0), (64, 32, 0),
+             (32, 32, 0), (32, 16, 0), (16, 16, 0), (16, 16, 1), (128, 128, 2)}
+    assert seen == every, every ^ seen
+    for mnk, plan in BIG_EXACT_CASES:
+        p = rbi.matmul_bi_plan(*mnk)
+        assert (p["first"], p["n1"], p["second"]) == plan, mnk
+
+
+def test_matmul_grid_bound():
+    # more 16 x 16 tiles than one launch's threads can cover: refused before any launch
+    L = rbi.lib()
+    p = ctypes.c_void_p(16)
+    st = L.matmul_bi(p, 1 << 20, p, 1 << 20, p, 1 << 17, 1, 1 << 17, 1 << 17, 1 << 20, None)
+    assert st == -2
+    buf = (ctypes.c_int64 * 7)()
+    assert L.matmul_bi_plan(4096, 9216, 4096, buf) == 0 and buf[3] == 8192
+    assert L.matmul_bi_plan(0, 9216, 4096, buf) == -1

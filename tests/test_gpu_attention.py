@@ -1,6 +1,6 @@
 """GPU tests of decode_attn_bi / decode_attn_tuned / kv_append: parity with the
-CPU oracle (per row, max|out - ref| <= 2e-2 * RMS(ref) beyond the bf16 rounding of
-the output; see tests.conftest.attn_tol) and bitwise invariance across
+CPU oracle (per row, max|out - RNE_bf16(ref)| <= 2e-2 * RMS(ref row); see
+tests.conftest.attn_tol) and bitwise invariance across
 batch size, neighbours, order, page placement, grid extent (max_kv_len), KV
 growth across split boundaries and chunked versus unchunked prefill.
 """
@@ -35,10 +35,6 @@ def _oracle(q, kv, scale, rows=None):
                               synth.bf16_bits(kv.v_cache.cpu()), bt, lens, scale)
 
 
-def _tol_ok(out, ref):
-    return attn_tol(out, ref)
-
-
 def _run(fn, q, kv, max_len, **kw):
     return fn(q, kv.k_cache, kv.v_cache, kv.block_table, kv.kv_lens, max_len, **kw)
 
@@ -50,7 +46,7 @@ def test_c1_tiny_parity_and_rows_bitwise():
     q = synth.normal((3, 4, 64), seed=100).to(DEV)
     scale = 1 / 8
     out = _run(rbi.decode_attn_bi, q, kv, 63, split_size=16, scale=scale)
-    ok, ratio, row = _tol_ok(out, _oracle(q, kv, scale))
+    ok, ratio, row = attn_tol(out, _oracle(q, kv, scale), name="c1")
     assert ok, (ratio, row)
     assert not torch.isnan(out.float()).any()
     for r in range(3):
@@ -76,7 +72,7 @@ def test_c4_heads_parity(lens):
     ref = _oracle(q, kv, scale)
     for fn, kw in ((rbi.decode_attn_bi, dict(split_size=256)), (rbi.decode_attn_tuned, {})):
         out = _run(fn, q, kv, max(lens), scale=scale, **kw)
-        ok, ratio, row = _tol_ok(out, ref)
+        ok, ratio, row = attn_tol(out, ref, name=f"{fn.__name__} {lens}")
         assert ok, (fn.__name__, ratio, row)
 
 
@@ -93,7 +89,7 @@ def test_shapes_and_split_sizes(d, hq, hkv, split):
     scale = 1 / math.sqrt(d)
     L = max(lens)
     out = _run(rbi.decode_attn_bi, q, kv, L, split_size=split, scale=scale)
-    ok, ratio, row = _tol_ok(out, _oracle(q, kv, scale))
+    ok, ratio, row = attn_tol(out, _oracle(q, kv, scale), name=f"d{d} hq{hq} hkv{hkv} S{split}")
     assert ok, (ratio, row)
     for r in (0, 2, 5):
         sub = synth.PagedKV(kv.k_cache, kv.v_cache, kv.block_table[r:r + 1].contiguous(),
@@ -122,17 +118,29 @@ def test_c4_full_batch_sampled_parity_and_batch_invariance():
     scale = 1 / math.sqrt(128)
     out = _run(rbi.decode_attn_bi, q, kv, 32768)
     rows = [0, 17, 100, 255]
-    ok, ratio, row = _tol_ok(out[rows], _oracle(q, kv, scale, rows=rows))
+    ok, ratio, row = attn_tol(out[rows], _oracle(q, kv, scale, rows=rows), name="c4 batch 256")
     assert ok, (ratio, row)
-    # every row alone and in random sub-batches gives the same bits
+    # every batch size 1..256: a seeded random subset of the requests in random order
+    # (so each row sits at a random position among random neighbours) gives every
+    # row the bits it has in the full batch
     rng = np.random.default_rng(synth.SEED_BATCH)
-    for B in (1, 2, 3, 7, 16, 64, 255):
+    bad = torch.zeros((), dtype=torch.int64, device=DEV)
+    o = torch.empty_like(out)
+    ws = torch.empty(rbi.decode_attn_workspace_size(256, 64, 128, 32768, 256), dtype=torch.uint8,
+                     device=DEV)
+    first_bad = None
+    for B in range(1, 257):
         members = synth.batch_members(256, B, seed=int(rng.integers(1 << 30)))
         idx = torch.tensor(members, device=DEV)
         sub = synth.PagedKV(kv.k_cache, kv.v_cache, kv.block_table[idx].contiguous(),
                             kv.kv_lens[idx].contiguous(), 16, 4, 128)
-        o = _run(rbi.decode_attn_bi, q[idx].contiguous(), sub, 32768)
-        assert torch.equal(o, out[idx]), B
+        _run(rbi.decode_attn_bi, q[idx].contiguous(), sub, 32768, out=o[:B], workspace=ws)
+        bad += (o[:B] != out[idx]).sum()
+        if B % 64 == 0:
+            if first_bad is None and int(bad):
+                first_bad = B
+            print(f"batch sizes 1..{B}: {int(bad)} differing elements", flush=True)
+    assert int(bad) == 0, f"first seen by batch {first_bad}"
 
 
 def test_grid_extent_and_page_placement_do_not_matter():
@@ -277,12 +285,17 @@ def test_tuned_twin_sensitivity():
     assert not torch.equal(full[0], one[0])
 
 
-def test_run_to_run_200():
+def test_run_to_run_1000():
+    # hidekazu-konishi.com sections 4.2 and 6.3: the same call 1000 times, every bit equal
     lens = synth.uniform_lengths(64, 1, 8192, seed=23)
     kv = _to(synth.paged_kv(lens, 4, 128, 16, max_pages=8192 // 16))
     q = synth.normal((64, 64, 128), seed=24).to(DEV)
     ref = _run(rbi.decode_attn_bi, q, kv, 8192)
+    out = torch.empty_like(ref)
+    ws = torch.empty(rbi.decode_attn_workspace_size(64, 64, 128, 8192, 256), dtype=torch.uint8,
+                     device=DEV)
     diff = torch.zeros((), dtype=torch.int64, device=DEV)
-    for _ in range(200):
-        diff += (_run(rbi.decode_attn_bi, q, kv, 8192) != ref).sum()
+    for _ in range(1000):
+        _run(rbi.decode_attn_bi, q, kv, 8192, out=out, workspace=ws)
+        diff += (out != ref).sum()
     assert int(diff) == 0

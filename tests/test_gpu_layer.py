@@ -210,6 +210,49 @@ def test_graph_replay_equals_eager_steps(weights):
 
 
 
+def test_graph_replay_matches_oracle(weights):
+    # The step captured as a HIP graph at batch 16, rows at mixed positions over a
+    # seeded random cache (lengths 1..1600, several across the 256- and 512-token
+    # split boundaries), replayed for 3 steps with the greedy tokens fed back.  Each
+    # replay's logits on sampled rows are checked against the fp64 layer oracle, which
+    # holds the same cache bits, at the composed layer's bar, and each row's greedy
+    # token must be the oracle's unless the oracle's own top two are within that bar.
+    B, steps, pages_per = 16, 3, 100
+    rng = np.random.default_rng(29)
+    table = np.stack([_table(list(range(r * pages_per, (r + 1) * pages_per))) for r in range(B)])
+    pos = rng.integers(0, 1596, B)
+    pos[:5] = [0, 254, 255, 511, 1595]
+    tok = rng.integers(0, CFG.vocab, B)
+    layer = DecodeLayer(CFG, weights, num_pages=B * pages_per)
+    layer.k_cache.copy_(synth.normal(tuple(layer.k_cache.shape), seed=90, device=DEV))
+    layer.v_cache.copy_(synth.normal(tuple(layer.v_cache.shape), seed=91, device=DEV))
+    dims = LayerDims(CFG.hidden, CFG.num_q_heads, CFG.num_kv_heads, CFG.head_dim,
+                     CFG.intermediate, CFG.vocab, CFG.eps, CFG.page_size)
+    orc = DenseLayerOracle(dims, {k: synth.bf16_bits(v) for k, v in weights.items()},
+                           num_pages=B * pages_per)
+    orc.k_cache[...] = synth.bf16_bits(layer.k_cache)
+    orc.v_cache[...] = synth.bf16_bits(layer.v_cache)
+    g = GraphedStep(layer, table, pos, tok)
+    sample = [0, 1, 2, 3, 4, 9]
+    tol = 5e-2
+    for i in range(steps):
+        lg_g, tk_g = g.step(tok, pos + i)
+        torch.cuda.synchronize()
+        o_lg, o_tok = orc.step(tok, table, pos + i, logit_rows=sample)
+        gl = lg_g[sample].double().cpu().numpy()
+        gt = tk_g.cpu().numpy()
+        for j, r in enumerate(sample):
+            o = o_lg[j].astype(np.float64)
+            rms = np.sqrt(np.mean(o ** 2))
+            err = np.abs(gl[j] - o)
+            print(f"graph replay {i} row {r} (position {pos[r] + i}): max err / RMS = "
+                  f"{err.max() / rms:.4g}, mean err / RMS = {err.mean() / rms:.4g}", flush=True)
+            assert err.max() <= tol * rms, (i, r, err.max(), rms)
+            assert err.mean() <= 5e-3 * rms, (i, r, err.mean(), rms)
+            assert int(gt[r]) == int(o_tok[j]) or o[int(o_tok[j])] - o[int(gt[r])] <= tol * rms
+        tok = gt
+
+
 def test_prompt_chunks_through_prefill_equal_decode_rows(weights):
     # A step whose rows mix decode rows of other requests with prompt chunks (runs
     # of consecutive positions of one request) sends the chunks to the prefill

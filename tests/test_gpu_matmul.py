@@ -19,6 +19,8 @@ OPROJ = (4096, 8192)   # [N, K] of o_proj
 def _tol_ok(c: torch.Tensor, ref: np.ndarray) -> tuple:
     err = np.abs(c.double().cpu().numpy() - ref).max()
     rms = np.sqrt(np.mean(ref ** 2))
+    print(f"parity matmul {tuple(c.shape)}: max|C - ref| / RMS = {err / rms:.4g}; bar 0.02",
+          flush=True)
     return err <= 2e-2 * rms, err, rms
 
 
@@ -38,16 +40,21 @@ def test_c1_parity_and_rows_bitwise_across_batch():
         assert torch.equal(rbi.matmul_bi(Ag[r:r + 1].contiguous(), Wg)[0], outs[8][r])
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 512, 256), (17, 4096, 4096), (130, 260, 1032),
-                                   (257, 9216, 512), (64, 128, 8), (300, 260, 576),
-                                   (600, 1004, 128),
-                                   # the register-streaming tile (M <= 16, <= 256 tiles of 16
-                                   # columns): ragged N, a single k step, a step count that
-                                   # is not a multiple of its ring, M at its limit
-                                   (5, 20, 32), (3, 36, 4000), (16, 4096, 352),
-                                   # the two-wave 32 x 32 tile (33 <= M <= 64, N <= 4096):
-                                   # ragged M and N
-                                   (40, 100, 320), (64, 4096, 1024)])
+SMALL_EXACT_CASES = [(1, 512, 256), (17, 4096, 4096), (130, 260, 1032),
+                     (257, 9216, 512), (64, 128, 8), (300, 260, 576),
+                     (600, 1004, 128),
+                     # the register-streaming tile (M <= 16, <= 256 tiles of 16
+                     # columns): ragged N, a single k step, a step count that
+                     # is not a multiple of its ring, M at its limit
+                     (5, 20, 32), (3, 36, 4000), (16, 4096, 352),
+                     # the two-wave 32 x 32 tile (33 <= M <= 64, N <= 4096):
+                     # ragged M and N
+                     (40, 100, 320), (64, 4096, 1024),
+                     # the 32 x 16 LDS tile (9 <= M <= 32, more than 1024 16 x 16 tiles)
+                     (24, 24576, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL_EXACT_CASES)
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_integer_inputs_exact(M, N, K, out_dtype):
     # integers in [-4, 4]: every partial sum is an integer below 2^24, so fp32 is exact
@@ -62,6 +69,42 @@ def test_integer_inputs_exact(M, N, K, out_dtype):
         assert np.array_equal(synth.bf16_bits(c), oracle.round_bf16(ref))
     ct = rbi.matmul_tuned(A.to(DEV), W.to(DEV), out_dtype=out_dtype).cpu()
     assert torch.equal(ct, c)
+
+
+# Full-size integer cases through the multi-wave tiles the large-M plans launch: each
+# (M, N, K) with the launches matmul_bi makes for it (matmul_bi_plan).  Together with
+# the cases of test_integer_inputs_exact they reach every tile shape of the plan table
+# (checked on the CPU by tests/test_capi_host.py).
+BIG_EXACT_CASES = [
+    ((4096, 9216, 4096), ((256, 256, 0), 8192, (128, 128, 0))),   # QKV: column split
+    ((2048, 9216, 4096), ((256, 256, 0), 8192, (128, 64, 0))),    # other right-hand tile
+    ((4096, 4096, 8192), ((256, 256, 0), 4096, None)),            # o_proj: one launch
+    ((768, 9216, 4096), ((256, 128, 0), 9216, None)),
+    ((1280, 4096, 8192), ((128, 128, 0), 4096, None)),
+    ((509, 4096, 8192), ((128, 64, 0), 4096, None)),
+]
+
+
+@pytest.mark.parametrize("mnk,plan", BIG_EXACT_CASES, ids=lambda v: str(v))
+def test_integer_exact_big_tiles(mnk, plan):
+    # integers in [-4, 4]: |partial sums| <= 16 K <= 2^17, exact in fp32 in any order,
+    # so sampled rows must equal the oracle bit for bit; rows on both sides of tile
+    # boundaries, every column (both sides of the column split included)
+    M, N, K = mnk
+    got = rbi.matmul_bi_plan(M, N, K)
+    assert (got["first"], got["n1"], got["second"]) == plan
+    A = synth.integer_valued((M, K), seed=7 * M + K)
+    W = synth.integer_valued((N, K), seed=N + 3)
+    Ag, Wg = A.to(DEV), W.to(DEV)
+    c32 = rbi.matmul_bi(Ag, Wg, out_dtype=torch.float32)
+    c16 = rbi.matmul_bi(Ag, Wg)
+    rng = np.random.default_rng(M + N)
+    rows = sorted({0, 1, 15, 16, 63, 64, 127, 128, 255, 256, M // 2, M - 2, M - 1} |
+                  set(rng.integers(0, M, 3).tolist()))
+    rows = [r for r in rows if r < M]
+    ref = oracle.matmul(synth.bf16_bits(A[rows]), synth.bf16_bits(W))
+    assert np.array_equal(c32[rows].double().cpu().numpy(), ref)
+    assert np.array_equal(synth.bf16_bits(c16[rows]), oracle.round_bf16(ref))
 
 
 @pytest.mark.parametrize("shape", [QKV, OPROJ])

@@ -91,7 +91,8 @@ def test_prefill_equals_decode_rows(d, hq, hkv, split, start, tokens):
     pick = {0, tokens - 1} | set(rng.integers(0, tokens, size=6).tolist())
     pick |= {t for t in range(tokens) if (start + t + 1) % split in (0, 1)}
     rows = sorted(pick)[:24]
-    ok, ratio, worst = attn_tol(out[rows], p.oracle_rows([start + t for t in rows]))
+    ok, ratio, worst = attn_tol(out[rows], p.oracle_rows([start + t for t in rows]),
+                                name=f"prefill start={start} tokens={tokens}")
     assert ok, (ratio, rows[worst])
 
 
@@ -122,9 +123,20 @@ def test_chunked_prefill_is_bitwise_unchunked():
     assert not torch.isnan(full.float()).any()
 
 
-def test_prefill_run_to_run():
-    p = Prompt(900, 4, 64, 128, seed=51)
-    p.append(0, 900)
-    first = p.prefill(100, 900, 256)
-    for _ in range(5):
-        assert torch.equal(p.prefill(100, 900, 256), first)
+def test_prefill_run_to_run_1000():
+    # hidekazu-konishi.com sections 4.2 and 6.3: 1000 calls, every bit equal; a chunk
+    # on each schedule (fused: 800 tokens; split: 40 tokens after a 900-token prefix)
+    p = Prompt(940, 4, 64, 128, seed=51)
+    p.append(0, 940)
+    for a, b in ((100, 900), (900, 940)):
+        first = p.prefill(a, b, 256)
+        out = torch.empty_like(first)
+        ws = torch.empty(max(16, rbi.prefill_attn_workspace_size(b - a, 64, 4, 128, a, 256)),
+                         dtype=torch.uint8, device=DEV)
+        q = p.q[a:b].contiguous()
+        diff = torch.zeros((), dtype=torch.int64, device=DEV)
+        for _ in range(1000):
+            rbi.prefill_attn_bi(q, p.kc, p.vc, p.pages, a, 256, scale=1 / math.sqrt(128),
+                                out=out, workspace=ws)
+            diff += (out != first).sum()
+        assert int(diff) == 0, (a, b)
