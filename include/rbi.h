@@ -190,7 +190,9 @@ int matmul_tuned(const void *A, int64_t lda, const void *W, int64_t ldw, void *C
  *               the split partials: with nsmax = ceil(max_kv_len / split_size) and
  *               item = (r * num_q_heads + h) * nsmax + s, fp32 acc[item][head_dim]
  *               first, then fp32 (m, l)[item][2] (m in log2 units: scale *
- *               log2(e) * <q, k>, l the sum of the bf16-rounded 2^(score - m));
+ *               log2(e) * <q, k>, l the sum of the weights 2^(score - m) as the
+ *               P.V product takes them: each weight split into two bf16 parts, so
+ *               16 significant bits);
  *               splits s >= ceil(kv_lens[r] / split_size) are not written
  * Supported: head_dim 64 or 128; page_size 16; split_size a positive multiple of
  * page_size, at most 1024; num_q_heads % num_kv_heads == 0 with a group of 1..16

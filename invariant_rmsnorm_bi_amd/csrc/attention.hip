@@ -17,8 +17,10 @@
 //     lane group q = lane/16 carrying d = q*D/4 + 8c .. +7 in step c);
 //   * log2-domain softmax in fp32: s2 = score * (scale * log2 e), masked to -inf
 //     past the split end; per wave a running max m and, per lane, a running sum
-//     of the bf16-rounded p = 2^(s2 - m) (the same p that feeds the product);
-//   * acc[head][d] += P . V with the same MFMA (P operand A, V operand B).  V pages
+//     of p = 2^(s2 - m) as the product sees it: p is split into two bf16 parts,
+//     hi = bf16(p) and lo = bf16(p - hi), so it keeps 16 significant bits;
+//   * acc[head][d] += HI . V + LO . V with the same MFMA (P operand A, V operand B;
+//     two MFMAs into one accumulator).  V pages
 //     are stored head-dim-major ([d][token]), so one 16-byte load of a V page row is
 //     exactly the operand fragment (8 consecutive tokens at one d): no staging;
 //   * the eight waves' (m, l, acc) are combined in wave order 0 .. 7
@@ -171,9 +173,10 @@ __device__ __forceinline__ void mask_runs(const uint4 (&src)[AttnK<D>::DB], int 
 // unless the pair is full).  Tokens past `keep` in a run get weight 0.
 //   scores  s2 = (K . q) * scale * log2(e), fp32, -inf when masked
 //   m_new   = max(m_run, max_j s2_j)           (per head, over the 32 tokens)
-//   p_j     = bf16(2^(s2_j - m_new))
+//   e_j     = 2^(s2_j - m_new),  p_j = hi_j + lo_j with hi_j = bf16(e_j),
+//             lo_j = bf16(e_j - hi_j)
 //   l_run   = fma(l_run, 2^(m_run - m_new), sum of this lane's p_j in token order)
-//   acc     = acc * 2^(m_run - m_new) + P . V  (bf16 MFMA, fp32 accumulate)
+//   acc     = acc * 2^(m_run - m_new) + HI . V + LO . V  (bf16 MFMA, fp32 accumulate)
 // FRESH: the state is the initial (-inf, 0, 0), for which the rescaling is the
 // identity on zeros and is skipped (same bits).  full: every token of the pair
 // is live (keep = 8 in every run), so the score mask is all-pass and skipped.
@@ -208,17 +211,23 @@ __device__ __forceinline__ void pair_update(const PairFrag<D> &f, const uint4 (&
     const float m_new = FRESH ? mloc : fmaxf(m_run, mloc);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
 
-    uint32_t pw[2][2];  // bf16 p, two per word, token order within the run
+    // p enters the bf16 P.V product as two bf16 parts, p_hi = bf16(p) and
+    // p_lo = bf16(p - p_hi) (two MFMAs into one accumulator), so the weights carry
+    // 16 significant bits instead of 8; l sums the same p_hi + p_lo (exact in fp32).
+    uint32_t pw[2][2], pl[2][2];  // bf16 p_hi / p_lo, two per word, token order in the run
     float psum = 0.f;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
         for (int j = 0; j < 4; j += 2) {
-            const uint32_t w =
-                cvt_pk_bf16(exp2_hw(sv[b][j] - m_use), exp2_hw(sv[b][j + 1] - m_use));
-            psum += __uint_as_float(w << 16);
-            psum += __uint_as_float(w & 0xffff0000u);
+            const float e0 = exp2_hw(sv[b][j] - m_use), e1 = exp2_hw(sv[b][j + 1] - m_use);
+            const uint32_t w = cvt_pk_bf16(e0, e1);
+            const float h0 = __uint_as_float(w << 16), h1 = __uint_as_float(w & 0xffff0000u);
+            const uint32_t wl = cvt_pk_bf16(e0 - h0, e1 - h1);
+            psum += h0 + __uint_as_float(wl << 16);
+            psum += h1 + __uint_as_float(wl & 0xffff0000u);
             pw[b][j / 2] = w;
+            pl[b][j / 2] = wl;
         }
     }
     if constexpr (FRESH) {
@@ -237,9 +246,12 @@ __device__ __forceinline__ void pair_update(const PairFrag<D> &f, const uint4 (&
     m_run = m_new;
 
     const bf16x8_t pf = as_bf16x8(make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
+    const bf16x8_t pfl = as_bf16x8(make_uint4(pl[0][0], pl[0][1], pl[1][0], pl[1][1]));
 #pragma unroll
-    for (int db = 0; db < P::DB; ++db)
+    for (int db = 0; db < P::DB; ++db) {
         acc[db] = mfma_16x16x32_bf16(pf, as_bf16x8(v[db]), acc[db]);
+        acc[db] = mfma_16x16x32_bf16(pfl, as_bf16x8(v[db]), acc[db]);
+    }
 }
 
 // True when page pair pr of the split [t0, t1) is live in every token.
@@ -326,8 +338,11 @@ __device__ __forceinline__ float fold_step(float acc, float al, float be, float 
 }
 
 // MULTI: splits longer than 2 * PAGE * WAVES tokens (several page pairs per wave).
+// Its loop keeps a pair, the accumulators and the loop state live at once, more
+// than the 128 registers of two workgroups per compute unit at head_dim 128, so
+// it runs one workgroup per unit (no spills); the one-pair kernel runs two.
 template <int D, bool MULTI>
-__global__ __launch_bounds__(512, 4) void attn_split_kernel(
+__global__ __launch_bounds__(512, MULTI ? 2 : 4) void attn_split_kernel(
     const uint16_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_table,
     int64_t bt_stride, const int32_t *__restrict__ kv_lens, int hq, int hkv, int S,
