@@ -21,7 +21,7 @@
  *  - All tensor pointers are DEVICE pointers (hipMalloc'd or from a framework
  *    allocator) unless an argument says "host".  The caller owns all memory.
  *    The library never allocates, frees or synchronises, and keeps no mutable
- *    global state.
+ *    global state other than the device scratch of decode_attn_bi_noalloc.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is
  *    enqueued asynchronously on it; results are ready when the stream is.
  *  - Return value: RBI_OK (0) or a negative status.  Arguments are validated
@@ -209,6 +209,33 @@ int decode_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, con
                    void *out, int64_t out_row_stride, int64_t rows, int num_q_heads,
                    int num_kv_heads, int head_dim, int page_size, int split_size, int max_kv_len,
                    float scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * decode_attn_bi_noalloc: decode_attn_bi for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same function, kernels and bits as decode_attn_bi; the
+ * split partials go to a static device array of the library instead of a
+ * caller's workspace.  The caller still passes inputs and outputs.
+ *  - Limit: decode_attn_workspace_size(rows, num_q_heads, head_dim, max_kv_len,
+ *    split_size) <= RBI_NOALLOC_SCRATCH_BYTES (128 MiB), else RBI_EWORKSPACE with
+ *    nothing enqueued (e.g. 64 query heads of 128 at split 256: rows *
+ *    ceil(max_kv_len / 256) <= 4032).
+ *  - The array is held by every device the library runs on until the process
+ *    ends.  The first call on a device looks up its address there (no
+ *    allocation); make that first call outside a graph capture.
+ *  - Every call on one device shares that device's array, which keeps the last
+ *    call's partials.  Calls that overlap on one device (two streams at once)
+ *    race and give undefined results; calls in one stream are ordered.
+ *  - Nothing in the array needs to start at zero.  No hipMalloc, hipFree or
+ *    other allocating routine is called.
+ * Other arguments, requirements and errors as decode_attn_bi.
+ */
+#define RBI_NOALLOC_SCRATCH_BYTES (128u << 20)
+int decode_attn_bi_noalloc(const void *q, int64_t q_row_stride, const void *k_cache,
+                           const void *v_cache, const int32_t *block_table, int64_t bt_stride,
+                           const int32_t *kv_lens, void *out, int64_t out_row_stride, int64_t rows,
+                           int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                           int split_size, int max_kv_len, float scale, void *stream);
 
 /*
  * decode_attn_tuned: same function, but the split size is chosen from the

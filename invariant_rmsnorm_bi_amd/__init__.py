@@ -26,7 +26,8 @@ import torch
 __all__ = [
     "RbiError", "lib", "lib_path", "build_info", "rmsnorm_bi", "rmsnorm_tuned", "matmul_bi", "matmul_tuned",
     "matmul_tuned_workspace_size", "matmul_bi_plan", "decode_attn_bi", "decode_attn_tuned",
-    "decode_attn_workspace_size", "decode_attn_tuned_split_size", "prefill_attn_bi",
+    "decode_attn_workspace_size", "decode_attn_tuned_split_size", "decode_attn_bi_noalloc",
+    "NOALLOC_SCRATCH_BYTES", "prefill_attn_bi",
     "prefill_attn_workspace_size", "sample_gumbel", "sample_gumbel_workspace_size",
     "kv_append", "embed",
     "residual_add", "swiglu", "argmax_rows", "EXPORTS",
@@ -41,7 +42,7 @@ RBI_F32, RBI_BF16 = 0, 1
 EXPORTS = (
     "rbi_status_string", "rbi_abi_version", "rbi_build_info", "rmsnorm_bi", "rmsnorm_tuned", "matmul_bi",
     "matmul_tuned", "matmul_tuned_workspace_size", "matmul_bi_plan", "decode_attn_workspace_size",
-    "decode_attn_bi", "decode_attn_tuned_split_size", "decode_attn_tuned",
+    "decode_attn_bi", "decode_attn_bi_noalloc", "decode_attn_tuned_split_size", "decode_attn_tuned",
     "prefill_attn_workspace_size", "prefill_attn_bi", "sample_gumbel_workspace_size",
     "sample_gumbel", "kv_append",
     "rbi_embed", "rbi_residual_add", "rbi_swiglu", "rbi_argmax_rows",
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
         "decode_attn_workspace_size": ([i64, i32, i32, i32, i32], sz),
         "decode_attn_bi": ([p, i64, p, p, p, i64, p, p, i64, i64, i32, i32, i32, i32, i32, i32,
                             f32, p, sz, p], i32),
+        "decode_attn_bi_noalloc": ([p, i64, p, p, p, i64, p, p, i64, i64, i32, i32, i32, i32,
+                                    i32, i32, f32, p], i32),
         "decode_attn_tuned_split_size": ([i64, i32, i32, p], i32),
         "decode_attn_tuned": ([p, i64, p, p, p, i64, p, p, p, i64, i64, i32, i32, i32, i32, i32,
                                f32, p, sz, p], i32),
@@ -298,6 +301,26 @@ def decode_attn_bi(q, k_cache, v_cache, block_table, kv_lens, max_kv_len: int,
                               float(scale), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream())
     _check(st, "decode_attn_bi")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # RBI_NOALLOC_SCRATCH_BYTES
+
+
+def decode_attn_bi_noalloc(q, k_cache, v_cache, block_table, kv_lens, max_kv_len: int,
+                           split_size: int = 256, scale: float | None = None,
+                           out=None) -> torch.Tensor:
+    """decode_attn_bi with its split partials in the library's static device scratch
+    (no workspace, nothing allocated by the library; pass `out` to allocate nothing
+    here either).  Same bits as decode_attn_bi.  Calls that overlap on one device
+    race on the shared scratch."""
+    rows, hq, hkv, d, page, out = _attn_prep(q, k_cache, v_cache, block_table, kv_lens, out)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    st = lib().decode_attn_bi_noalloc(_ptr(q), _lead_stride(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(block_table), _lead_stride(block_table), _ptr(kv_lens),
+                                      _ptr(out), _lead_stride(out), rows, hq, hkv, d, page,
+                                      split_size, max_kv_len, float(scale), _stream())
+    _check(st, "decode_attn_bi_noalloc")
     return out
 
 

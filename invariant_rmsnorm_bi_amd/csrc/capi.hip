@@ -5,9 +5,39 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "launch.h"
 
+// Device scratch of decode_attn_bi_noalloc: its split partials, for callers that
+// cannot allocate.  Each device the library runs on holds one copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: kernels get the address hipGetSymbolAddress returns for it.
+static __device__ __align__(256) unsigned char scratch[RBI_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_dev[kMaxDevices];  // device address of `scratch`, per device, once looked up
+
+// The device address of `scratch` on the calling thread's current device: looked
+// up once per device (with that device current) and kept; allocates nothing.
+int scratch_for_current_device(void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return RBI_ELAUNCH;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return RBI_ELAUNCH;
+        scratch_dev[dev] = p;
+    }
+    *ptr = scratch_dev[dev];
+    return RBI_OK;
+}
 
 inline bool aligned16(const void *p)
 {
@@ -234,6 +264,33 @@ int decode_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, con
     return attn_common(q, q_row_stride, k_cache, v_cache, block_table, bt_stride, kv_lens, out,
                        out_row_stride, rows, num_q_heads, num_kv_heads, head_dim, page_size,
                        split_size, max_kv_len, scale, workspace, workspace_bytes, stream);
+}
+
+int decode_attn_bi_noalloc(const void *q, int64_t q_row_stride, const void *k_cache,
+                           const void *v_cache, const int32_t *block_table, int64_t bt_stride,
+                           const int32_t *kv_lens, void *out, int64_t out_row_stride, int64_t rows,
+                           int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                           int split_size, int max_kv_len, float scale, void *stream)
+{
+    const int st = check_attn(q, q_row_stride, k_cache, v_cache, block_table, bt_stride, kv_lens,
+                              out, out_row_stride, rows, num_q_heads, num_kv_heads, head_dim,
+                              page_size, split_size, max_kv_len);
+    if (st != RBI_OK || rows == 0)
+        return st;
+    // every partial the merge reads is written by the same call first, so nothing in
+    // the scratch has to start at zero
+    if (rbi::attn_workspace_bytes(rows, num_q_heads, head_dim, max_kv_len, split_size) >
+        (size_t)RBI_NOALLOC_SCRATCH_BYTES)
+        return RBI_EWORKSPACE;
+    void *ws = nullptr;
+    const int sp = scratch_for_current_device(&ws);
+    if (sp != RBI_OK)
+        return sp;
+    const rbi::AttnArgs a{(const uint16_t *)q, q_row_stride, (const uint16_t *)k_cache,
+                          (const uint16_t *)v_cache, block_table, bt_stride, kv_lens,
+                          (uint16_t *)out, out_row_stride, rows, num_q_heads, num_kv_heads,
+                          head_dim, page_size, split_size, max_kv_len, scale, (float *)ws};
+    return launched(rbi::launch_decode_attn(a, stream_of(stream)));
 }
 
 size_t prefill_attn_workspace_size(int64_t tokens, int num_q_heads, int num_kv_heads,

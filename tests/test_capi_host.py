@@ -249,3 +249,20 @@ def test_matmul_grid_bound():
     buf = (ctypes.c_int64 * 7)()
     assert L.matmul_bi_plan(4096, 9216, 4096, buf) == 0 and buf[3] == 8192
     assert L.matmul_bi_plan(0, 9216, 4096, buf) == -1
+
+
+def test_decode_attn_noalloc_limit():
+    # more partials than the static scratch holds (256 rows of 64 heads at 32768
+    # tokens: 545 MB > 128 MiB): refused on the host before the device is touched
+    L = rbi.lib()
+    f = ctypes.c_void_p(FAKE)
+    assert rbi.decode_attn_workspace_size(256, 64, 128, 32768, 256) > rbi.NOALLOC_SCRATCH_BYTES
+    st = L.decode_attn_bi_noalloc(f, 64 * 128, f, f, f, 2048, f, f, 64 * 128, 256, 64, 4, 128, 16,
+                                  256, 32768, 0.1, None)
+    assert st == EWORKSPACE
+    # the usual argument checks come first
+    st = L.decode_attn_bi_noalloc(f, 64 * 128, f, f, f, 2047, f, f, 64 * 128, 256, 64, 4, 128, 16,
+                                  256, 32768, 0.1, None)
+    assert st == EINVAL
+    assert L.decode_attn_bi_noalloc(f, 64 * 128, f, f, f, 2048, f, f, 64 * 128, 0, 64, 4, 128, 16,
+                                    256, 32768, 0.1, None) == OK

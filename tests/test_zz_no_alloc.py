@@ -1,0 +1,47 @@
+"""decode_attn_bi_noalloc, the entry point for callers that cannot allocate: its
+split partials live in the library's static device scratch instead of a caller's
+workspace.  Checked bit for bit against decode_attn_bi (the same kernels with a
+caller's workspace) on two calls in a row, the second with a smaller input, and
+its size limit.  Collected last (the name sorts last), so a failure here cannot
+hide the other GPU tests.
+"""
+import pytest
+import torch
+
+import invariant_rmsnorm_bi_amd as rbi
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _case(lens, hq, hkv, d, lmax, seed):
+    # block tables as wide as max_kv_len needs (ceil(max_kv_len / 16) entries)
+    kv = synth.paged_kv(lens, hkv, d, 16, seed=seed, device=DEV, max_pages=-(-lmax // 16))
+    q = synth.normal((len(lens), hq, d), seed=seed + 100, device=DEV)
+    return q, kv
+
+
+def test_noalloc_equals_decode_attn_bi_on_two_calls():
+    # call 1: 64 requests of U{1..8192} tokens (64 x 64 heads x 32 splits x 130 floats,
+    # 68 MB of the 128 MiB scratch); call 2, smaller: 5 requests at head_dim 64 whose
+    # partials overwrite only the start of what call 1 left there
+    cases = [(synth.uniform_lengths(64, 1, 8192, seed=41), 64, 4, 128, 8192, 256),
+             ([1, 17, 300, 1000, 2500], 32, 4, 64, 2500, 128)]
+    outs = []
+    for lens, hq, hkv, d, lmax, split in cases:
+        print(f"noalloc case rows={len(lens)} hq={hq} hkv={hkv} d={d} max_kv_len={lmax} "
+              f"split={split}", flush=True)
+        q, kv = _case(lens, hq, hkv, d, lmax, seed=len(lens))
+        need = rbi.decode_attn_workspace_size(len(lens), hq, d, lmax, split)
+        assert need <= rbi.NOALLOC_SCRATCH_BYTES
+        ref = rbi.decode_attn_bi(q, kv.k_cache, kv.v_cache, kv.block_table, kv.kv_lens, lmax,
+                                 split)
+        out = torch.full_like(ref, float("nan"))
+        rbi.decode_attn_bi_noalloc(q, kv.k_cache, kv.v_cache, kv.block_table, kv.kv_lens, lmax,
+                                   split, out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        outs.append((out, ref))
+    for out, ref in outs:  # neither output was touched by the later call
+        assert torch.equal(out, ref)
