@@ -249,6 +249,26 @@ def vendor_gemm_us(wl: Workload):
     return out
 
 
+def ceilings(wl: Workload):
+    """Read + write reference rates for RMSNorm on this machine: the library's plain
+    streaming copy (rbi_stream_copy, one 16-byte chunk per thread) over the same
+    four rotating 64 MiB input / output sets the RMSNorm leg uses, with ordinary and
+    with non-temporal stores, graph-replayed like the per-kernel graph_us."""
+    out = {}
+    nbytes = RMS_ROWS * H * 2
+    for nt in (False, True):
+        it = iter(range(1 << 30))
+
+        def rot(nt=nt, it=it):
+            i = next(it) % SETS
+            rbi.stream_copy(wl.x[i], wl.y[i], nontemporal=nt)
+        us = graph_time_fn(rot) * 1e3
+        out["copy_64MiB_nt" if nt else "copy_64MiB"] = {
+            "us": round(us, 2), "GB/s": round(2 * nbytes / us / 1e3, 1),
+            "frac_hbm_peak": round(2 * nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def twin_points(wl: Workload):
     """(name, bi_fn, tuned_fn) at the slowdown points: RMSNorm batch sizes, matmul M
     for both projections, attention batch sizes."""
@@ -258,7 +278,8 @@ def twin_points(wl: Workload):
         y = wl.y[0][:B]
         pts.append((f"rmsnorm B={B}",
                     lambda x=x, y=y: rbi.rmsnorm_bi(x, wl.w_ln, 1e-6, out=y),
-                    lambda x=x, y=y: rbi.rmsnorm_tuned(x, wl.w_ln, 1e-6, out=y)))
+                    lambda x=x, y=y: rbi.rmsnorm_tuned(x, wl.w_ln, 1e-6, out=y),
+                    B < 1024))  # the twin's workgroup-per-row tree below 1024 rows
     for nm, A, W, C, K in (("qkv", wl.a_qkv[0], wl.w_qkv[0], wl.c_qkv, QKV[1]),
                            ("oproj", wl.a_o[0], wl.w_o[0], wl.c_o, OPROJ[1])):
         for M in (1, 7, 64, 127, 256, 509, 1024, 2039, 4096):
@@ -267,7 +288,8 @@ def twin_points(wl: Workload):
             pts.append((f"matmul {nm} M={M}",
                         lambda A=A[:M], W=W, C=C[:M]: rbi.matmul_bi(A, W, out=C),
                         lambda A=A[:M], W=W, C=C[:M], ws=ws: rbi.matmul_tuned(A, W, out=C,
-                                                                              workspace=ws)))
+                                                                              workspace=ws),
+                        rbi.matmul_tuned_differs(M, W.shape[0], K)))
     kv = wl.kv
     for B in (1, 16, 64, 256):
         bt, ln, q = kv.block_table[:B], kv.kv_lens[:B], wl.q[:B]
@@ -281,7 +303,8 @@ def twin_points(wl: Workload):
                         q, kv.k_cache, kv.v_cache, bt, ln, LMAX, SPLIT, out=out, workspace=wl.ws),
                     lambda bt=bt, ln=ln, q=q, out=out, host=host, ws_t=ws_t: rbi.decode_attn_tuned(
                         q, kv.k_cache, kv.v_cache, bt, ln, LMAX, kv_lens_host=host, out=out,
-                        workspace=ws_t)))
+                        workspace=ws_t),
+                    split_t != SPLIT))
     return pts
 
 
@@ -289,27 +312,26 @@ def layer_points():
     """End-to-end decode step of the dense layer (hidden 4096, 64/4 heads of 128,
     SwiGLU 12288, lm_head 151936, greedy argmax) built from the bi kernels versus
     the same layer built from the tuned twins, at batch sizes 1, 16, 64 and 128;
-    each request has its own pages and a KV length ~ U{1..4096} (the cache holds
-    seeded random K/V).  Wall clock per step (host scheduling included), median of
-    10 after 3 warmup steps, eager and replayed as a captured HIP graph (same
-    kernels, no per-launch host cost); the graphed pair prices determinism on the
-    device work, the eager pair includes each side's host cost."""
+    each request has its own pages and a KV length ~ U{1..32768} (the decode-layer
+    workload's lengths; the cache holds seeded random K/V, shared by the two layers).
+    Wall clock per step (host scheduling included), median of 10 after 3 warmup
+    steps, eager and replayed as a captured HIP graph (same kernels, no per-launch
+    host cost); the graphed pair prices determinism on the device work, the eager
+    pair includes each side's host cost."""
     from invariant_rmsnorm_bi_amd.layer import DecodeLayer, GraphedStep, LayerConfig
     cfg = LayerConfig()
     w = synth.dense_layer_weights(cfg.hidden, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
                                   cfg.intermediate, cfg.vocab, device=DEV)
     rng = np.random.default_rng(synth.SEED_BATCH)
-    Bmax, lmax = 128, 4096
+    Bmax, lmax = 128, cfg.max_kv_len
     pages_per = lmax // cfg.page_size
-    layers = {}
-    for tuned in (False, True):
-        layers[tuned] = DecodeLayer(cfg, w, num_pages=Bmax * pages_per, device=DEV, tuned=tuned)
-    kc = synth.normal(tuple(layers[False].k_cache.shape), seed=60, device=DEV)
-    vc = synth.normal(tuple(layers[False].v_cache.shape), seed=61, device=DEV)
-    for tuned in (False, True):
-        layers[tuned].k_cache.copy_(kc)
-        layers[tuned].v_cache.copy_(vc)
-    del kc, vc
+    layers = {False: DecodeLayer(cfg, w, num_pages=Bmax * pages_per, device=DEV),
+              True: DecodeLayer(cfg, w, num_pages=1, device=DEV, tuned=True)}
+    for seed, c in ((60, layers[False].k_cache), (61, layers[False].v_cache)):
+        for i in range(0, c.shape[0], 8192):  # seeded N(0,1) K/V, drawn in slices
+            c[i:i + 8192].copy_(synth.normal(tuple(c[i:i + 8192].shape),
+                                             seed=seed * 1000003 + i, device=DEV))
+    layers[True].k_cache, layers[True].v_cache = layers[False].k_cache, layers[False].v_cache
     table = np.zeros((Bmax, cfg.max_kv_len // cfg.page_size), dtype=np.int32)
     for r in range(Bmax):
         table[r, :pages_per] = np.arange(r * pages_per, (r + 1) * pages_per)
@@ -632,6 +654,8 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+    log("timing the streaming-copy reference")
+    ceil = ceilings(wl)
 
     twins = None
     if not args.no_twins:
@@ -644,12 +668,17 @@ def main():
             log(f"vendor GEMM timing failed: {e}")
         log("timing the tuned twins")
         pts = []
-        for name, fbi, ftu in twin_points(wl):
+        for name, fbi, ftu, differs in twin_points(wl):
             tb, tt = graph_time_fn(fbi), graph_time_fn(ftu)
             pts.append({"point": name, "bi_us": round(tb * 1e3, 2), "tuned_us": round(tt * 1e3, 2),
-                        "slowdown_pct": round((tb / tt - 1) * 100, 2)})
+                        "slowdown_pct": round((tb / tt - 1) * 100, 2),
+                        "schedule_differs": bool(differs)})
         mean = float(np.mean([p["slowdown_pct"] for p in pts]))
+        diff = [p["slowdown_pct"] for p in pts if p["schedule_differs"]]
         twins = {"points": pts, "mean_slowdown_pct": round(mean, 2),
+                 "mean_slowdown_pct_where_schedules_differ": (round(float(np.mean(diff)), 2)
+                                                              if diff else None),
+                 "points_where_schedules_differ": len(diff),
                  "unit": "time increase of bi over tuned, percent",
                  "timing": "device time per call: 20 calls replayed as one HIP graph, median of 10",
                  "pages_context": PAGES_COST_CONTEXT}
@@ -687,7 +716,8 @@ def main():
                                 "[4096,8192]x[4096,8192]^T + kv_append + decode_attn_bi batch 256 "
                                 "(64q/4kv heads, d128, page 16, split 256, L~U{1..32768})"),
                    "step_bytes": step_bytes, "buffer_sets": SETS},
-        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "twins": twins,
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "ceilings": ceil,
+        "twins": twins,
         "prefill": prefill, "sampling": sampling,
         "fingerprint": fingerprint(),
     }

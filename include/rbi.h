@@ -146,6 +146,9 @@ int matmul_bi_plan(int64_t M, int64_t N, int64_t K, int64_t *plan);
  * (0 means none is needed; NULL is then allowed).
  */
 size_t matmul_tuned_workspace_size(int64_t M, int64_t N, int64_t K);
+/* 1 when matmul_tuned runs a different schedule (and so, in general, different
+ * bits) than matmul_bi for (M, N, K), else 0; host only. */
+int matmul_tuned_differs(int64_t M, int64_t N, int64_t K);
 int matmul_tuned(const void *A, int64_t lda, const void *W, int64_t ldw, void *C, int64_t ldc,
                  int c_dtype, int64_t M, int64_t N, int64_t K, void *workspace,
                  size_t workspace_bytes, void *stream);
@@ -368,6 +371,15 @@ int rbi_swiglu(const void *gu, int64_t gu_row_stride, void *out, int64_t out_row
  * entries are skipped (a row of only NaN yields 0). */
 int rbi_argmax_rows(const float *x, int64_t x_row_stride, int64_t rows, int64_t n,
                     int32_t *out, void *stream);
+
+/* -------------------------------------------------------------------------- */
+/* Measurement aid                                                             */
+/* -------------------------------------------------------------------------- */
+/* rbi_stream_copy: dst[0, bytes) = src[0, bytes), one 16-byte chunk per thread,
+ * with ordinary or (nontemporal != 0) non-temporal stores: the read + write rate
+ * a read-once write-once kernel such as rmsnorm_bi is judged against.  bytes a
+ * multiple of 16, both pointers 16-byte aligned, the ranges must not overlap. */
+int rbi_stream_copy(const void *src, void *dst, int64_t bytes, int nontemporal, void *stream);
 
 #ifdef __cplusplus
 }

@@ -25,12 +25,12 @@ import torch
 
 __all__ = [
     "RbiError", "lib", "lib_path", "build_info", "rmsnorm_bi", "rmsnorm_tuned", "matmul_bi", "matmul_tuned",
-    "matmul_tuned_workspace_size", "matmul_bi_plan", "decode_attn_bi", "decode_attn_tuned",
+    "matmul_tuned_workspace_size", "matmul_bi_plan", "matmul_tuned_differs", "decode_attn_bi", "decode_attn_tuned",
     "decode_attn_workspace_size", "decode_attn_tuned_split_size", "decode_attn_bi_noalloc",
     "NOALLOC_SCRATCH_BYTES", "prefill_attn_bi",
     "prefill_attn_workspace_size", "sample_gumbel", "sample_gumbel_workspace_size",
     "kv_append", "embed",
-    "residual_add", "swiglu", "argmax_rows", "EXPORTS",
+    "residual_add", "swiglu", "argmax_rows", "stream_copy", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,11 +41,12 @@ RBI_F32, RBI_BF16 = 0, 1
 # every symbol include/rbi.h declares
 EXPORTS = (
     "rbi_status_string", "rbi_abi_version", "rbi_build_info", "rmsnorm_bi", "rmsnorm_tuned", "matmul_bi",
-    "matmul_tuned", "matmul_tuned_workspace_size", "matmul_bi_plan", "decode_attn_workspace_size",
+    "matmul_tuned", "matmul_tuned_workspace_size", "matmul_bi_plan", "matmul_tuned_differs",
+    "decode_attn_workspace_size",
     "decode_attn_bi", "decode_attn_bi_noalloc", "decode_attn_tuned_split_size", "decode_attn_tuned",
     "prefill_attn_workspace_size", "prefill_attn_bi", "sample_gumbel_workspace_size",
     "sample_gumbel", "kv_append",
-    "rbi_embed", "rbi_residual_add", "rbi_swiglu", "rbi_argmax_rows",
+    "rbi_embed", "rbi_residual_add", "rbi_swiglu", "rbi_argmax_rows", "rbi_stream_copy",
 )
 
 
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
         "matmul_bi": ([p, i64, p, i64, p, i64, i32, i64, i64, i64, p], i32),
         "matmul_tuned_workspace_size": ([i64, i64, i64], sz),
         "matmul_bi_plan": ([i64, i64, i64, p], i32),
+        "matmul_tuned_differs": ([i64, i64, i64], i32),
         "matmul_tuned": ([p, i64, p, i64, p, i64, i32, i64, i64, i64, p, sz, p], i32),
         "decode_attn_workspace_size": ([i64, i32, i32, i32, i32], sz),
         "decode_attn_bi": ([p, i64, p, p, p, i64, p, p, i64, i64, i32, i32, i32, i32, i32, i32,
@@ -100,6 +102,7 @@ def lib() -> ctypes.CDLL:
         "rbi_residual_add": ([p, p, p, i64, p], i32),
         "rbi_swiglu": ([p, i64, p, i64, i64, i64, p], i32),
         "rbi_argmax_rows": ([p, i64, i64, i64, p, p], i32),
+        "rbi_stream_copy": ([p, p, i64, i32, p], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -220,6 +223,11 @@ def matmul_bi_plan(M: int, N: int, K: int) -> dict:
     _check(lib().matmul_bi_plan(M, N, K, buf), "matmul_bi_plan")
     v = list(buf)
     return {"first": tuple(v[0:3]), "n1": v[3], "second": tuple(v[4:7]) if v[4] else None}
+
+
+def matmul_tuned_differs(M: int, N: int, K: int) -> bool:
+    """Whether matmul_tuned runs another schedule than matmul_bi for (M, N, K)."""
+    return bool(lib().matmul_tuned_differs(M, N, K))
 
 
 def matmul_tuned_workspace_size(M: int, N: int, K: int) -> int:
@@ -494,3 +502,14 @@ def argmax_rows(x: torch.Tensor, out=None) -> torch.Tensor:
     st = lib().rbi_argmax_rows(_ptr(x), _row_stride(x), rows, n, _ptr(out), _stream())
     _check(st, "rbi_argmax_rows")
     return out
+
+
+def stream_copy(src: torch.Tensor, dst: torch.Tensor, nontemporal: bool = False) -> None:
+    """dst <- src (same byte size, contiguous) by the library's plain streaming copy
+    kernel: the read + write reference rate for RMSNorm (a measurement aid)."""
+    _need_cuda(src, dst)
+    nbytes = src.numel() * src.element_size()
+    if not (src.is_contiguous() and dst.is_contiguous()) or dst.numel() * dst.element_size() != nbytes:
+        raise RbiError("stream_copy needs two contiguous tensors of one byte size")
+    _check(lib().rbi_stream_copy(_ptr(src), _ptr(dst), nbytes, int(nontemporal), _stream()),
+           "rbi_stream_copy")

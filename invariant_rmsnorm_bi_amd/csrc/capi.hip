@@ -203,6 +203,13 @@ int matmul_bi_plan(int64_t M, int64_t N, int64_t K, int64_t *plan)
     return RBI_OK;
 }
 
+int matmul_tuned_differs(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 1 || N < 1 || K < 8 || K % 8 || N % 4)
+        return 0;
+    return rbi::matmul_tuned_splits(M, N, K) > 1 ? 1 : 0;
+}
+
 size_t matmul_tuned_workspace_size(int64_t M, int64_t N, int64_t K)
 {
     if (M <= 0 || N <= 0 || K <= 0)
@@ -477,6 +484,19 @@ int rbi_argmax_rows(const float *x, int64_t x_row_stride, int64_t rows, int64_t 
     if (rows > (int64_t)0x7fffffff)
         return RBI_EUNSUPPORTED;
     return launched(rbi::launch_argmax(x, x_row_stride, rows, n, out, stream_of(stream)));
+}
+
+int rbi_stream_copy(const void *src, void *dst, int64_t bytes, int nontemporal, void *stream)
+{
+    if (bytes < 0 || bytes % 16)
+        return RBI_EINVAL;
+    if (bytes == 0)
+        return RBI_OK;
+    if (!src || !dst || !aligned16(src) || !aligned16(dst))
+        return RBI_EINVAL;
+    if (bytes / 16 > ((int64_t)1 << 32) * 255)
+        return RBI_EUNSUPPORTED;
+    return launched(rbi::launch_stream_copy(src, dst, bytes, nontemporal != 0, stream_of(stream)));
 }
 
 }  // extern "C"

@@ -153,6 +153,25 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float *x, int64_t xs
     }
 }
 
+// Plain streaming copy, one 16-byte chunk per thread: the read + write reference
+// a read-once write-once kernel such as RMSNorm is measured against.
+template <bool NT>
+__global__ __launch_bounds__(256) void stream_copy_kernel(const uint4 *__restrict__ src,
+                                                          uint4 *__restrict__ dst, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n)
+        return;
+    const uint4 v = src[i];
+    if constexpr (NT) {
+        typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w},
+                                    reinterpret_cast<u32x4_t *>(dst + i));
+    } else {
+        dst[i] = v;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_embed(const uint16_t *table, int64_t vocab, int64_t hidden, const int32_t *ids,
@@ -188,6 +207,21 @@ hipError_t launch_argmax(const float *x, int64_t xs, int64_t rows, int64_t n, in
         argmax_kernel<true><<<dim3((unsigned)rows), dim3(1024), 0, s>>>(x, xs, n, out);
     else
         argmax_kernel<false><<<dim3((unsigned)rows), dim3(1024), 0, s>>>(x, xs, n, out);
+    return hipGetLastError();
+}
+
+}  // namespace rbi
+
+namespace rbi {
+
+hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, bool nt, hipStream_t s)
+{
+    const int64_t n = bytes / 16;
+    const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+    if (nt)
+        stream_copy_kernel<true><<<grid, block, 0, s>>>((const uint4 *)src, (uint4 *)dst, n);
+    else
+        stream_copy_kernel<false><<<grid, block, 0, s>>>((const uint4 *)src, (uint4 *)dst, n);
     return hipGetLastError();
 }
 

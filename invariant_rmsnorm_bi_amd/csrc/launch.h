@@ -95,6 +95,7 @@ hipError_t launch_residual_add(const uint16_t *a, const uint16_t *b, uint16_t *o
                                hipStream_t s);
 hipError_t launch_swiglu(const uint16_t *gu, int64_t gs, uint16_t *out, int64_t os, int64_t rows,
                          int64_t inter, hipStream_t s);
+hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, bool nt, hipStream_t s);
 hipError_t launch_argmax(const float *x, int64_t xs, int64_t rows, int64_t n, int32_t *out,
                          hipStream_t s);
 

@@ -121,8 +121,9 @@ __device__ __forceinline__ void unpack_chunk(const uint4 &q, float *v)
     }
 }
 
-// A full chunk of y = round((x * rsq) * w), with w already loaded.
-template <bool BF16>
+// A full chunk of y = round((x * rsq) * w), with w already loaded.  NT: a
+// non-temporal store (y is written once and not read back by this kernel).
+template <bool BF16, bool NT = false>
 __device__ __forceinline__ void store_full_chunk(char *row, int64_t c, const float *v,
                                                  const float *w, float rsq)
 {
@@ -143,7 +144,13 @@ __device__ __forceinline__ void store_full_chunk(char *row, int64_t c, const flo
         q.z = __float_as_uint(o[2]);
         q.w = __float_as_uint(o[3]);
     }
-    *reinterpret_cast<uint4 *>(row + c * 16) = q;
+    if constexpr (NT) {
+        typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(u32x4_t{q.x, q.y, q.z, q.w},
+                                    reinterpret_cast<u32x4_t *>(row + c * 16));
+    } else {
+        *reinterpret_cast<uint4 *>(row + c * 16) = q;
+    }
 }
 
 // Fixed pairwise tree over the per-slot partials of one lane.
@@ -211,8 +218,8 @@ __global__ __launch_bounds__(64 * RPW) void rmsnorm_wave_kernel(const char *x, i
 // ascending step order, the slot tree and the butterfly.  After a second barrier
 // every wave writes its own chunks with that rsq (letting every wave repeat the
 // reduction instead read the row from LDS NWV times and was 6-14 % slower).
-// Rows of at most 64 * CPL chunks.
-template <bool BF16, int CPL, int NWV>
+// Rows of at most 64 * CPL chunks.  NT: y is stored non-temporally (large batches).
+template <bool BF16, int CPL, int NWV, bool NT>
 __global__ __launch_bounds__(64 * NWV) void rmsnorm_split_kernel(const char *x, int64_t xs,
                                                                  const char *__restrict__ w,
                                                                  char *y, int64_t ys,
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(64 * NWV) void rmsnorm_split_kernel(const char *x, 
         if (c < nfull) {
             float wv8[VEC];
             unpack_chunk<BF16>(wq[j], wv8);
-            store_full_chunk<BF16>(yr, c, v[j], wv8, rsq);
+            store_full_chunk<BF16, NT>(yr, c, v[j], wv8, rsq);
         } else if (tail && c == nfull) {
             store_chunk<BF16>(yr, w, c, H, v[j], rsq);
         }
@@ -390,6 +397,12 @@ hipError_t launch_rmsnorm_wave(const void *x, int64_t xs, const void *w, void *y
     // 14.8, 8192 rows 26.2 vs 28.9; one wave per row, four rows per workgroup:
     // 28.6 us at 8192 rows).  Rows longer than 64 * 8 chunks take the two-pass
     // wave kernel, four rows per workgroup from 4096 rows on.
+    // Beyond 1024 rows y is stored non-temporally: back-to-back calls over four
+    // 8192-row sets 28.1 -> 23.3 us (4.8 -> 5.8 TB/s), 4096 rows 14.0 -> 12.7 us;
+    // same bits.  (Right after a 1 GiB copy has left the caches full of dirty
+    // lines, one call is slower that way, 29.4 -> 32.0 us at 8192 rows; at up to
+    // 1024 rows, the batch sizes whose output the next kernel reads at once,
+    // the stores stay ordinary.)
     const int64_t vec = bf16 ? 8 : 4;
     const bool in_regs = (hidden + vec - 1) / vec <= 64 * 8;
     if (!in_regs && rows >= 4096) {
@@ -411,18 +424,18 @@ hipError_t launch_rmsnorm_wave(const void *x, int64_t xs, const void *w, void *y
     } else if (rows <= 1024) {
         const dim3 grid((unsigned)rows), block(512);
         if (bf16)
-            rmsnorm_split_kernel<true, 8, 8><<<grid, block, 0, s>>>(
+            rmsnorm_split_kernel<true, 8, 8, false><<<grid, block, 0, s>>>(
                 (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
         else
-            rmsnorm_split_kernel<false, 8, 8><<<grid, block, 0, s>>>(
+            rmsnorm_split_kernel<false, 8, 8, false><<<grid, block, 0, s>>>(
                 (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
     } else {
         const dim3 grid((unsigned)rows), block(256);
         if (bf16)
-            rmsnorm_split_kernel<true, 8, 4><<<grid, block, 0, s>>>(
+            rmsnorm_split_kernel<true, 8, 4, true><<<grid, block, 0, s>>>(
                 (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
         else
-            rmsnorm_split_kernel<false, 8, 4><<<grid, block, 0, s>>>(
+            rmsnorm_split_kernel<false, 8, 4, true><<<grid, block, 0, s>>>(
                 (const char *)x, xs, (const char *)w, (char *)y, ys, rows, hidden, eps);
     }
     return hipGetLastError();
