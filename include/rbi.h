@@ -190,13 +190,15 @@ int matmul_tuned(const void *A, int64_t lda, const void *W, int64_t ldw, void *C
  *               workspace only -- results do not depend on it
  *  workspace    >= decode_attn_workspace_size(rows, num_q_heads, head_dim,
  *               max_kv_len, split_size) bytes, 16-byte aligned.  On return it holds
- *               the split partials: with nsmax = ceil(max_kv_len / split_size) and
- *               item = (r * num_q_heads + h) * nsmax + s, fp32 acc[item][head_dim]
- *               first, then fp32 (m, l)[item][2] (m in log2 units: scale *
- *               log2(e) * <q, k>, l the sum of the weights 2^(score - m) as the
- *               P.V product takes them: each weight split into two bf16 parts, so
- *               16 significant bits);
- *               splits s >= ceil(kv_lens[r] / split_size) are not written
+ *               the split partials: with nsmax = ceil(max_kv_len / split_size),
+ *               G = num_q_heads / num_kv_heads and query head h = g * G + hh, the
+ *               partial of (row r, head h, split s) is the (D + 4)-float slot
+ *               (((r * num_kv_heads + g) * nsmax + s) * G + hh): fp32 acc[0 .. D),
+ *               then m (log2 units: scale * log2(e) * <q, k>), l (the sum of the
+ *               weights 2^(score - m) as the P.V product takes them: each weight
+ *               split into two bf16 parts, so 16 significant bits) and two zeros.
+ *               One split's G slots are one contiguous block.  Splits
+ *               s >= ceil(kv_lens[r] / split_size) are not written
  * Supported: head_dim 64 or 128; page_size 16; split_size a positive multiple of
  * page_size, at most 1024; num_q_heads % num_kv_heads == 0 with a group of 1..16
  * query heads; rows <= 65535 and ceil(max_kv_len / split_size) * num_kv_heads
@@ -222,7 +224,7 @@ int decode_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, con
  *  - Limit: decode_attn_workspace_size(rows, num_q_heads, head_dim, max_kv_len,
  *    split_size) <= RBI_NOALLOC_SCRATCH_BYTES (128 MiB), else RBI_EWORKSPACE with
  *    nothing enqueued (e.g. 64 query heads of 128 at split 256: rows *
- *    ceil(max_kv_len / 256) <= 4032).
+ *    ceil(max_kv_len / 256) <= 3971).
  *  - The array is held by every device the library runs on until the process
  *    ends.  The first call on a device looks up its address there (no
  *    allocation); make that first call outside a graph capture.
@@ -285,7 +287,7 @@ int decode_attn_tuned(const void *q, int64_t q_row_stride, const void *k_cache,
  *  workspace      >= prefill_attn_workspace_size(...) bytes, 16-byte aligned; that
  *                 size is 0 (no workspace; NULL allowed) when the chunk has enough
  *                 tokens to fill the GPU with token blocks, otherwise the split
- *                 partials are staged there as in decode_attn_bi (item layout
+ *                 partials are staged there as in decode_attn_bi (slot layout
  *                 with rows = tokens, nsmax = ceil((start_pos+tokens)/split_size))
  * Supported: head_dim 64 or 128; page_size 16; split_size a positive multiple of
  * page_size, at most 256 (one page pair per wave); a group of 1..16 query heads

@@ -192,12 +192,13 @@ def test_kv_growth_across_split_boundaries():
     for L in range(240, 2101):
         lens1 = torch.tensor([L], dtype=torch.int32, device=DEV)
         alone = rbi.decode_attn_bi(q, kc, vc, bt_pp_d, lens1, LMAX, S, workspace=ws1)
-        acc = ws1[: HQ * nsmax * D * 4].view(torch.float32).view(HQ, nsmax, D)
+        # the row's partials: [kv head, split, query head of the group, acc | m | l | pad]
+        slots = ws1.view(torch.float32).view(HKV, nsmax, HQ // HKV, D + 4)
         for k in range(L // S):
             if k in done:
-                assert torch.equal(acc[:, k], done[k]), (L, k)
+                assert torch.equal(slots[:, k], done[k]), (L, k)
             else:
-                done[k] = acc[:, k].clone()
+                done[k] = slots[:, k].clone()
         B = int(rng.integers(2, 33))
         pos = int(rng.integers(0, B))
         mem = rng.choice(32, size=B - 1, replace=False)
