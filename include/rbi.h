@@ -138,12 +138,15 @@ int matmul_bi(const void *A, int64_t lda, const void *W, int64_t ldw, void *C, i
 int matmul_bi_plan(int64_t M, int64_t N, int64_t K, int64_t *plan);
 
 /*
- * matmul_tuned: same function.  Chooses split-K from (M, N, K) so that small-M
- * problems fill the chip; split partials are reduced in ascending split order by
- * a second kernel (deterministic run to run, but the K partition -- and so the
- * bits -- changes with M: [P1] section 5.4, "split reduction, also known as
- * split-K").  Needs `workspace` of matmul_tuned_workspace_size(M, N, K) bytes
- * (0 means none is needed; NULL is then allowed).
+ * matmul_tuned: same function, shape-tuned.  Chooses a tile shape and a split-K
+ * count from (M, N, K) by a table measured on MI355X ([P1] section 5.4, "split
+ * reduction, also known as split-K"): where splitting K into 2 or 4 equal ranges
+ * beat matmul_bi's plan (long-K projections from M = 9 to 768, QKV-wide N near
+ * M = 128, very wide N at M <= 16) the ranges' fp32 partials are added in
+ * ascending order by a second kernel; elsewhere it runs matmul_bi's plan.  Run to
+ * run deterministic, but the K partition -- and so the bits -- changes with M.
+ * Needs `workspace` of matmul_tuned_workspace_size(M, N, K) bytes (0 means none
+ * is needed; NULL is then allowed).
  */
 size_t matmul_tuned_workspace_size(int64_t M, int64_t N, int64_t K);
 /* 1 when matmul_tuned runs a different schedule (and so, in general, different

@@ -43,6 +43,13 @@ hipError_t launch_matmul_bi(const MatmulArgs &a, hipStream_t s);
 // split-K twin: `splits` partial products over equal K ranges into fp32 workspace
 // [splits, M, N], then an ascending-order reduction into C.
 hipError_t launch_matmul_splitk(const MatmulArgs &a, int splits, float *ws, hipStream_t s);
+// The twin's tile shape (an index of the tile table; -1: matmul_bi's own choice)
+// and split-K count (1: matmul_bi's plan unchanged).
+struct TwinPlan {
+    int tile;
+    int split;
+};
+TwinPlan plan_matmul_tuned(int64_t M, int64_t N, int64_t K);
 int matmul_tuned_splits(int64_t M, int64_t N, int64_t K);
 
 // attention.hip

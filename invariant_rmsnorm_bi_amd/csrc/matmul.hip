@@ -759,37 +759,50 @@ hipError_t launch_matmul_bi(const MatmulArgs &a, hipStream_t s)
     return launch_tile_shape(p.t2, right, s);
 }
 
-// Split count of the twin.  With K a multiple of 32 it takes the tile shape the
-// invariant path would pick and cuts K into 2, 4, 8 or 16 equal ranges (each a
-// multiple of 32, at least 256 deep) until the workgroups fill the chip: ~1024 of
-// the one-wave small-M tiles, 256 of the bigger ones, whose partials only pay off
-// when their tiles leave half of the compute units idle.  Otherwise the 128x128
-// tile kernel's count.
+// The twin's schedule: a tile shape and a split-K count, picked from (M, N, K) by a
+// table measured on MI355X (graph-replayed device time on the decode layer's
+// projection shapes, every pipelined tile shape x splits 1, 2, 4 at M = 1 .. 4096):
+// wherever a split beat matmul_bi's own plan by a clear margin it is taken, and
+// everywhere else the twin runs matmul_bi's plan unchanged.  Winning splits:
+//  * long K with few output columns (N <= 4096, K >= 8192: o_proj, the down
+//    projection): from M = 9 on, K in 2 or 4 ranges (o_proj M = 64: 23.4 -> 17.3
+//    us; M = 127: 29.1 -> 21.4; M = 256: 33.6 -> 28.6; M = 509: 47.4 -> 44.0;
+//    down M = 127: 41.2 -> 27.7); at M <= 8 the register-streaming tile is faster
+//    than any split (o_proj M = 1: 11.4 vs 14.3 us), from M = 1024 no split wins;
+//  * QKV-wide N (8192 < N <= 12288, K <= 4096) at 81 <= M <= 160: 128 x 128 tiles
+//    in 2 ranges (M = 127: 27.3 -> 24.9 us);
+//  * very wide N (N >= 16384: gate/up) at M <= 16: 64 x 64 tiles in 2 ranges
+//    (M = 16: 34.9 -> 32.6 us).
+// The partition is a function of M, so the bits move with M.  With K % 32 != 0 the
+// 128 x 128 register-staged kernel splits K until its tiles fill the chip.
+TwinPlan plan_matmul_tuned(int64_t M, int64_t N, int64_t K)
+{
+    if (K % PK != 0) {
+        const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+        int splits = 1;
+        while (splits < 16 && tiles * splits < 256 && K / (splits * 2) >= 256)
+            splits *= 2;
+        return TwinPlan{-1, splits};
+    }
+    if (N <= 4096 && K >= 8192 && M > 8 && M <= 768) {
+        if (M <= 16)
+            return TwinPlan{6, 2};   // 16 x 16
+        if (M <= 64)
+            return TwinPlan{4, 4};   // 64 x 64
+        if (M <= 160)
+            return TwinPlan{3, 4};   // 128 x 64
+        return TwinPlan{2, M <= 384 ? 4 : 2};  // 128 x 128
+    }
+    if (N > 8192 && N <= 12288 && K <= 4096 && M > 80 && M <= 160)
+        return TwinPlan{2, 2};
+    if (N >= 16384 && K <= 4096 && M <= 16)
+        return TwinPlan{4, 2};
+    return TwinPlan{-1, 1};  // matmul_bi's plan
+}
+
 int matmul_tuned_splits(int64_t M, int64_t N, int64_t K)
 {
-    int64_t tiles, target = 256;
-    if (K % PK == 0) {
-        double c;
-        const int ti = best_tile(M, N, &c);
-        const TileCand &t = kTiles[ti];
-        tiles = ((M + t.tbm - 1) / t.tbm) * ((N + t.tbn - 1) / t.tbn);
-        if (ti == 8) {
-            return 1;  // the register-streaming tile: split-K over it measured slower
-                       // (o_proj M = 1: 15.4 us in 4 ranges vs 11.2 us unsplit)
-        } else if (ti >= kNumTiles) {
-            target = 1024;  // one-wave weight-streaming tiles: ~4 per compute unit
-        } else if (tiles > 128) {
-            // multi-wave tiles filling at least half of the compute units: the fp32
-            // partials' round trip costs more than the extra parallelism gains
-            return 1;
-        }
-    } else {
-        tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    }
-    int splits = 1;
-    while (splits < 16 && tiles * splits < target && K / (splits * 2) >= 256)
-        splits *= 2;
-    return splits;
+    return plan_matmul_tuned(M, N, K).split;
 }
 
 hipError_t launch_matmul_splitk(const MatmulArgs &a, int splits, float *ws, hipStream_t s)
@@ -804,7 +817,8 @@ hipError_t launch_matmul_splitk(const MatmulArgs &a, int splits, float *ws, hipS
     hipError_t e;
     if (a.K % PK == 0) {
         double c;
-        const int t = best_tile(a.M, a.N, &c);
+        const int pt = plan_matmul_tuned(a.M, a.N, a.K).tile;
+        const int t = pt >= 0 ? pt : best_tile(a.M, a.N, &c);
         MatmulArgs w = a;
         w.C = ws;
         w.ldc = a.N;

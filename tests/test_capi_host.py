@@ -70,18 +70,24 @@ def test_matmul_validation():
     assert f(FAKE, 64, FAKE, 64, FAKE + 8, 64, 1, 4, 64, 64, NULL) == EINVAL
     assert f(FAKE, 64, FAKE, 64, FAKE, 32, 1, 4, 64, 64, NULL) == EINVAL  # ldc < N
     g = rbi.lib().matmul_tuned
-    need = rbi.matmul_tuned_workspace_size(1, 9216, 4096)
-    assert need > 0
-    assert g(FAKE, 4096, FAKE, 4096, FAKE, 9216, 1, 1, 9216, 4096, NULL, need, NULL) == EWORKSPACE
-    assert g(FAKE, 4096, FAKE, 4096, FAKE, 9216, 1, 1, 9216, 4096, FAKE, need - 1, NULL) == EWORKSPACE
+    need = rbi.matmul_tuned_workspace_size(64, 4096, 8192)
+    assert need == 4 * 64 * 4096 * 4                    # four K ranges of fp32 partials
+    assert g(FAKE, 8192, FAKE, 8192, FAKE, 4096, 1, 64, 4096, 8192, NULL, need, NULL) == EWORKSPACE
+    assert g(FAKE, 8192, FAKE, 8192, FAKE, 4096, 1, 64, 4096, 8192, FAKE, need - 1, NULL) == EWORKSPACE
 
 
 def test_matmul_tuned_workspace_shape_dependence():
-    # the twin splits K only when the output tiles cannot fill the chip, and not
-    # over the register-streaming tile (at most one 16 x 16 tile per compute unit)
-    assert rbi.matmul_tuned_workspace_size(4096, 9216, 4096) == 0
-    assert rbi.matmul_tuned_workspace_size(1, 9216, 4096) > 0
-    assert rbi.matmul_tuned_workspace_size(1, 4096, 8192) == 0
+    # the twin's measured table: long-K projections split K from M = 9 to 768 (4 ranges
+    # up to 384 rows, 2 beyond), QKV-wide N in 2 ranges near M = 128, very wide N in 2
+    # ranges up to M = 16; elsewhere matmul_bi's plan (no workspace, same schedule)
+    for M, N, K, splits in ((1, 4096, 8192, 1), (8, 4096, 8192, 1), (9, 4096, 8192, 2),
+                            (64, 4096, 8192, 4), (384, 4096, 8192, 4), (385, 4096, 8192, 2),
+                            (768, 4096, 8192, 2), (769, 4096, 8192, 1), (127, 4096, 12288, 4),
+                            (127, 9216, 4096, 2), (64, 9216, 4096, 1), (4096, 9216, 4096, 1),
+                            (16, 24576, 4096, 2), (17, 24576, 4096, 1), (1, 9216, 4096, 1)):
+        assert rbi.matmul_tuned_workspace_size(M, N, K) == (splits * M * N * 4 if splits > 1
+                                                            else 0), (M, N, K)
+        assert rbi.matmul_tuned_differs(M, N, K) == (splits > 1), (M, N, K)
     assert rbi.matmul_tuned_workspace_size(0, 9216, 4096) == 0
 
 

@@ -182,23 +182,28 @@ def test_p1_batch_slice_example():
     one = rbi.matmul_bi(a[:1], W, out_dtype=torch.float32)
     full = rbi.matmul_bi(a, W, out_dtype=torch.float32)[:1]
     assert float((one - full).abs().max()) == 0.0
-    # the split-K twin is free to change with the batch: it splits K at M = 1 only.
-    # (At N = 4096 and M = 1 it runs the unsplit register-streaming tile, the same
-    # bits as matmul_bi, so the twin is shown on a linspace W twice as wide.)
-    W2 = synth.linspace_matrix(D, 2 * D, dtype=torch.bfloat16).T.contiguous().to(DEV)
+    # the split-K twin is free to change with the batch.  At this N = 4096, K = 4096 it
+    # runs matmul_bi's plan at both sizes, so the twin is shown on a linspace W four
+    # times as wide, where it splits K in two at M <= 16 and not at M = 2048.
+    W2 = synth.linspace_matrix(D, 4 * D, dtype=torch.bfloat16).T.contiguous().to(DEV)
+    assert rbi.matmul_tuned_differs(1, 4 * D, D) and not rbi.matmul_tuned_differs(B, 4 * D, D)
     t_one = rbi.matmul_tuned(a[:1], W2, out_dtype=torch.float32)
     t_full = rbi.matmul_tuned(a, W2, out_dtype=torch.float32)[:1]
     assert float((t_one - t_full).abs().max()) > 0.0, "inputs lack the power to show a change"
 
 
-def test_tuned_twin_sensitivity_normal_inputs():
-    N, K = QKV  # the twin splits K at M = 1 here (not at o_proj's N = 4096)
+@pytest.mark.parametrize("shape,m_small", [(OPROJ, 64), (QKV, 127)])
+def test_tuned_twin_sensitivity_normal_inputs(shape, m_small):
+    # the twin splits K at these M (o_proj: four ranges, QKV: two) and not at M = 4096,
+    # so a row's bits move with the batch; matmul_bi's do not
+    N, K = shape
+    assert rbi.matmul_tuned_differs(m_small, N, K) and not rbi.matmul_tuned_differs(4096, N, K)
     pool = synth.normal((4096, K), seed=41).to(DEV)
     W = synth.normal((N, K), std=0.02, seed=synth.SEED_WEIGHTS).to(DEV)
-    small = rbi.matmul_tuned(pool[:1], W, out_dtype=torch.float32)
+    small = rbi.matmul_tuned(pool[:m_small], W, out_dtype=torch.float32)[:1]
     big = rbi.matmul_tuned(pool, W, out_dtype=torch.float32)[:1]
     assert not torch.equal(small, big)
-    assert torch.equal(rbi.matmul_bi(pool[:1], W, out_dtype=torch.float32),
+    assert torch.equal(rbi.matmul_bi(pool[:m_small], W, out_dtype=torch.float32)[:1],
                        rbi.matmul_bi(pool, W, out_dtype=torch.float32)[:1])
 
 
