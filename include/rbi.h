@@ -170,11 +170,13 @@ int matmul_tuned(const void *A, int64_t lda, const void *W, int64_t ldw, void *C
  * j % page_size.  Split s covers tokens [s*split_size, min((s+1)*split_size, L));
  * the boundaries depend on nothing but L.  Per split the kernel forms a partial
  * (max m, sum l, accumulator acc) with bf16 MFMA products and fp32 softmax;
- * a second kernel folds the ceil(L / split_size) partials in ascending split
- * order with log-sum-exp rescaling (running maximum M; a partial (m, l_s, acc_s)
- * makes M' = max(M, m), l = l 2^(M - M') + 2^(m - M') l_s, acc likewise) and
- * rounds acc / l to bf16 once.  The
- * whole reduction tree is a function of L alone.
+ * partials are folded in ascending split order with log-sum-exp rescaling
+ * (running maximum M; a partial (m, l_s, acc_s) makes M' = max(M, m),
+ * l = l 2^(M - M') + 2^(m - M') l_s, acc likewise): for split sizes up to 256
+ * first within each group of 4 consecutive splits (splits 4k .. 4k+3), then the
+ * groups' partials by a second kernel; longer splits are each their own group.
+ * acc / l is rounded to bf16 once.  The whole reduction tree is a function of L
+ * alone.
  *
  *  q            [rows, num_q_heads, head_dim] bf16, row stride q_row_stride
  *               (head stride head_dim)
@@ -193,15 +195,16 @@ int matmul_tuned(const void *A, int64_t lda, const void *W, int64_t ldw, void *C
  *               workspace only -- results do not depend on it
  *  workspace    >= decode_attn_workspace_size(rows, num_q_heads, head_dim,
  *               max_kv_len, split_size) bytes, 16-byte aligned.  On return it holds
- *               the split partials: with nsmax = ceil(max_kv_len / split_size),
+ *               the group partials: with GS = 4 splits per group when split_size
+ *               <= 256 (else 1), np = ceil(ceil(max_kv_len / split_size) / GS),
  *               G = num_q_heads / num_kv_heads and query head h = g * G + hh, the
- *               partial of (row r, head h, split s) is the (D + 4)-float slot
- *               (((r * num_kv_heads + g) * nsmax + s) * G + hh): fp32 acc[0 .. D),
+ *               partial of (row r, head h, group s) is the (D + 4)-float slot
+ *               (((r * num_kv_heads + g) * np + s) * G + hh): fp32 acc[0 .. D),
  *               then m (log2 units: scale * log2(e) * <q, k>), l (the sum of the
  *               weights 2^(score - m) as the P.V product takes them: each weight
  *               split into two bf16 parts, so 16 significant bits) and two zeros.
- *               One split's G slots are one contiguous block.  Splits
- *               s >= ceil(kv_lens[r] / split_size) are not written
+ *               One group's G slots are one contiguous block.  Groups past
+ *               the row's last split are not written
  * Supported: head_dim 64 or 128; page_size 16; split_size a positive multiple of
  * page_size, at most 1024; num_q_heads % num_kv_heads == 0 with a group of 1..16
  * query heads; rows <= 65535 and ceil(max_kv_len / split_size) * num_kv_heads
@@ -227,7 +230,7 @@ int decode_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, con
  *  - Limit: decode_attn_workspace_size(rows, num_q_heads, head_dim, max_kv_len,
  *    split_size) <= RBI_NOALLOC_SCRATCH_BYTES (128 MiB), else RBI_EWORKSPACE with
  *    nothing enqueued (e.g. 64 query heads of 128 at split 256: rows *
- *    ceil(max_kv_len / 256) <= 3971).
+ *    ceil(max_kv_len / 1024) <= 3971, so 124 rows at 32768 tokens).
  *  - The array is held by every device the library runs on until the process
  *    ends.  The first call on a device looks up its address there (no
  *    allocation); make that first call outside a graph capture.
@@ -290,8 +293,8 @@ int decode_attn_tuned(const void *q, int64_t q_row_stride, const void *k_cache,
  *  workspace      >= prefill_attn_workspace_size(...) bytes, 16-byte aligned; that
  *                 size is 0 (no workspace; NULL allowed) when the chunk has enough
  *                 tokens to fill the GPU with token blocks, otherwise the split
- *                 partials are staged there as in decode_attn_bi (slot layout
- *                 with rows = tokens, nsmax = ceil((start_pos+tokens)/split_size))
+ *                 group partials are staged there as in decode_attn_bi (slot
+ *                 layout with rows = tokens and max_kv_len = start_pos + tokens)
  * Supported: head_dim 64 or 128; page_size 16; split_size a positive multiple of
  * page_size, at most 256 (one page pair per wave); a group of 1..16 query heads
  * per kv head; start_pos + tokens <= 2^30; 16-byte aligned q, out and caches,

@@ -8,10 +8,11 @@
 // splits grows with L.  The per-token reduction order is therefore a function
 // of the request's own length.
 //
-// Kernel 1 (one workgroup of 8 waves per (row, kv head, split)):
-//   * the split's 16-token pages are dealt to the waves in pairs (wave w takes
-//     pages 2w and 2w+1, then 2w+16, 2w+17, ... when the split is longer), each
-//     pair loaded in one burst;
+// Kernel 1 (one workgroup of 8 waves per (row, kv head, group of GROUP = 4
+// consecutive splits) for split sizes up to 256 tokens):
+//   * each split's 16-token pages are dealt to the waves in pairs (wave w takes
+//     pages 2w and 2w+1), each pair loaded in one burst; the next split's pair is
+//     requested before the current one is processed (two register buffers);
 //   * scores S^T[token][head] = K . q^T with v_mfma_f32_16x16x32_bf16 (K rows are
 //     operand A, the group's query heads operand B; head_dim is the k dimension,
 //     lane group q = lane/16 carrying d = q*D/4 + 8c .. +7 in step c);
@@ -24,16 +25,19 @@
 //     are stored head-dim-major ([d][token]), so one 16-byte load of a V page row is
 //     exactly the operand fragment (8 consecutive tokens at one d): no staging;
 //   * the eight waves' (m, l, acc) are combined in wave order 0 .. 7
-//     (M = max m, l = sum 2^(m_w - M) l_w, acc = sum 2^(m_w - M) acc_w), and the
-//     split's partial goes to the fp32 workspace.
-// Kernel 2 (one wave per (row, query head)): the same combine over the row's
-//   splits in ascending order, then out = bf16(acc / l).  It always runs, even
-//   for a single split.  The whole reduction tree is a function of L alone.
+//     (M = max m, l = sum 2^(m_w - M) l_w, acc = sum 2^(m_w - M) acc_w) into the
+//     split's partial, and the group's splits are folded in ascending order (the
+//     fold below); the group's partial goes to the fp32 workspace.
+//   Longer splits (up to 1024 tokens): one workgroup per (row, kv head, split),
+//   each wave walking several pairs; a group is then one split.
+// Kernel 2 (one wave per (row, query head)): the same ascending fold over the
+//   row's group partials, then out = bf16(acc / l).  It always runs, even for a
+//   single group.  The whole reduction tree -- pairs, waves, splits, groups -- is
+//   a function of L alone.
 // No atomics: the final combine is a separate ordered clean-up pass.
 //
 // The twin (decode_attn_tuned) runs the same kernels with a split size picked
-// from the batch shape -- the largest that still gives every compute unit work
-// -- which moves the split boundaries with the batch.
+// from the batch shape, which moves the split boundaries with the batch.
 #include "device.h"
 #include "launch.h"
 
@@ -42,6 +46,21 @@ namespace {
 
 constexpr int PAGE = 16;
 constexpr int WAVES = 8;   // waves per split workgroup
+// Splits per workgroup (and per workspace partial) for split sizes up to
+// 2 * PAGE * WAVES tokens.  Measured at the bench shape (batch 256, 64q/4kv, d128,
+// lengths U{1..32768}, split 256): one split per workgroup with its partial stored
+// 1.95 ms; groups of 4 at one workgroup per compute unit 1.80 ms (groups of 2:
+// 1.92, of 8: 1.85), with the next split's loads behind the current split's
+// pair update.  A workgroup's partial store costs far more than its bytes: the
+// same kernel with its stores removed ran 1.43 instead of 1.82 ms.
+constexpr int GROUP = 4;
+
+// Splits folded into one workspace partial: GROUP for splits of at most one page
+// pair per wave, else 1.  A function of the split size alone.
+constexpr int splits_per_partial(int split)
+{
+    return split <= 2 * PAGE * WAVES ? GROUP : 1;
+}
 // Row padding of the LDS stash of the waves' accumulators, in floats: a wave
 // writes head 4 * lane_group + j at d = 16 * db + lane % 16, so with rows of
 // D + 4 floats the four lane groups start 16 banks apart and a write is free
@@ -367,12 +386,13 @@ __device__ __forceinline__ void store_partial(float *dst, int dq, const float (&
         *reinterpret_cast<float4 *>(dst + D) = make_float4(M, l, 0.f, 0.f);
 }
 
-// MULTI: splits longer than 2 * PAGE * WAVES tokens (several page pairs per wave).
-// Its loop keeps a pair, the accumulators and the loop state live at once, more
-// than the 128 registers of two workgroups per compute unit at head_dim 128, so
-// it runs one workgroup per unit (no spills); the one-pair kernel runs two.
-template <int D, bool MULTI>
-__global__ __launch_bounds__(512, MULTI ? 2 : 4) void attn_split_kernel(
+// Splits longer than 2 * PAGE * WAVES tokens: one workgroup per (row, kv head,
+// split), wave w folding page pairs w, w + WAVES, ... with the running update.
+// The loop keeps a pair, the accumulators and the loop state live at once, more
+// than the 128 registers of two workgroups per compute unit at head_dim 128, so it
+// runs one workgroup per unit (no spills).
+template <int D>
+__global__ __launch_bounds__(512, 2) void attn_split_kernel(
     const uint16_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_table,
     int64_t bt_stride, const int32_t *__restrict__ kv_lens, int hq, int hkv, int S,
@@ -384,8 +404,7 @@ __global__ __launch_bounds__(512, MULTI ? 2 : 4) void attn_split_kernel(
     __shared__ __attribute__((aligned(16))) float c_acc[WAVES][16][D + CPAD];
 
     // grid x = split * hkv + kv head: the kv heads of one split are dispatched
-    // back to back, so the four 4 KiB head slices of each K and V page are read
-    // close together in time (3 % faster than split-fastest order, same bits)
+    // back to back, so the head slices of each K and V page are read close together
     const int s = (int)(blockIdx.x / (unsigned)hkv), g = (int)(blockIdx.x % (unsigned)hkv);
     const int64_t r = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -414,8 +433,6 @@ __global__ __launch_bounds__(512, MULTI ? 2 : 4) void attn_split_kernel(
     for (int db = 0; db < P::DB; ++db)
         acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Wave w takes the page pairs 2w, 2w+1 (+ 2*WAVES*i for splits longer than
-    // 2*WAVES pages), one pair per step.
     const int pairs = (valid_pages + 1) / 2;
     // first step's loads go out before the query is staged
     PairFrag<D> f;
@@ -431,28 +448,17 @@ __global__ __launch_bounds__(512, MULTI ? 2 : 4) void attn_split_kernel(
     }
     __syncthreads();  // q_lds ready
 
-    if constexpr (!MULTI) {
-        if (wave < pairs) {
-            const int keep = run_keep(wave, t0, t1, valid_pages, ln);
-            const bool full = pair_full(wave, t0, t1);
-            if (!full)
-                mask_runs<D>(f.v, keep, f.v);
-            pair_update<D, true>(f, f.v, keep, full, &q_lds[0][0], scale_log2, ln, m_run, l_run,
-                                 acc);
-        }
-    } else {
-        // (register budget: the query fragments are re-read from LDS every pair --
-        // the empty asm keeps them from being hoisted out of the loop -- and the
-        // all-pass mask of a full pair is applied anyway, which gives the same bits)
-        for (int pr = wave; pr < pairs; pr += WAVES) {
-            asm volatile("" ::: "memory");
-            if (pr != wave)
-                load_pair<D>(f, pr, my_page, valid_pages, k_cache, v_cache, hkv, g, ln);
-            const int keep = run_keep(pr, t0, t1, valid_pages, ln);
-            mask_runs<D>(f.v, keep, f.v);
-            pair_update<D, false>(f, f.v, keep, false, &q_lds[0][0], scale_log2, ln, m_run, l_run,
-                                  acc);
-        }
+    // (register budget: the query fragments are re-read from LDS every pair -- the
+    // empty asm keeps them from being hoisted out of the loop -- and the all-pass
+    // mask of a full pair is applied anyway, which gives the same bits)
+    for (int pr = wave; pr < pairs; pr += WAVES) {
+        asm volatile("" ::: "memory");
+        if (pr != wave)
+            load_pair<D>(f, pr, my_page, valid_pages, k_cache, v_cache, hkv, g, ln);
+        const int keep = run_keep(pr, t0, t1, valid_pages, ln);
+        mask_runs<D>(f.v, keep, f.v);
+        pair_update<D, false>(f, f.v, keep, false, &q_lds[0][0], scale_log2, ln, m_run, l_run,
+                              acc);
     }
 
     stash_wave<D>(m_run, l_run, acc, wave, ln, c_m, c_l, c_acc);
@@ -472,8 +478,118 @@ __global__ __launch_bounds__(512, MULTI ? 2 : 4) void attn_split_kernel(
     }
 }
 
-// One wave per (row, query head): the ascending fold of the row's split
-// partials.  The running maxima (prefix maxima over the splits, exact, so
+// Splits of at most 2 * PAGE * WAVES tokens (one page pair per wave): one
+// workgroup per (row, kv head, group of GROUP consecutive splits).  Each split's
+// partial is formed exactly as a split workgroup would (wave w's pair 2w, 2w + 1
+// with a fresh state, the wave combine in order) and folded into the group's
+// running (M, l, acc) held by the combining threads; the group's partial goes to
+// the workspace.  A wave requests its pair of split s + 1 as soon as its update of
+// split s is done, so the loads run under the stash, the combine and the fold
+// (requesting it before the update, into a second register buffer, measured
+// slower: 1.85 vs 1.80 ms at the bench shape).  The stash is double-buffered
+// (split s uses buffer s % 2), so one barrier per split suffices.  One workgroup
+// per compute unit.
+template <int D>
+__global__ __launch_bounds__(512, 2) void attn_group_kernel(
+    const uint16_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ k_cache,
+    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_table,
+    int64_t bt_stride, const int32_t *__restrict__ kv_lens, int hq, int hkv, int S,
+    int max_kv_len, int ngmax, float scale_log2, float *__restrict__ ws)
+{
+    using P = AttnK<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t q_lds[16][QROW<D>];
+    __shared__ float c_m[2][WAVES][16], c_l[2][WAVES][16];
+    __shared__ __attribute__((aligned(16))) float c_acc[2][WAVES][16][D + CPAD];
+
+    // grid x = group * hkv + kv head (the kv heads of a group back to back)
+    const int grp = (int)(blockIdx.x / (unsigned)hkv), g = (int)(blockIdx.x % (unsigned)hkv);
+    const int64_t r = blockIdx.z;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const PairLanes ln(lane);
+    const int split_pages = S / PAGE;
+    const int grp_pages = GROUP * split_pages;  // <= 64: one block-table entry per lane
+    const int row_pages = (max_kv_len + PAGE - 1) / PAGE;
+    const int32_t *btrow = block_table + r * bt_stride;
+    // the group's block-table entries, read before the length (clamped into the
+    // table row; entries past the row's last page are never used)
+    const int my_page = btrow[min(grp * grp_pages + min(lane, grp_pages - 1), row_pages - 1)];
+    const int L = clamp_len(kv_lens[r], max_kv_len);
+    const int nsplit = (L + S - 1) / S;
+    const int s0 = grp * GROUP;
+    if (s0 >= nsplit)
+        return;
+    const int s1 = min(s0 + GROUP, nsplit);
+    const int G = hq / hkv;
+
+    // pages of split s: entries (s - s0) * split_pages .. of the group's my_page
+    auto vpages = [&](int s) { return (min(s * S + S, L) - s * S + PAGE - 1) / PAGE; };
+    PairFrag<D> f;
+    auto load = [&](int s) {
+        if (wave < (vpages(s) + 1) / 2)
+            load_pair<D>(f, wave, __shfl(my_page, (lane + (s - s0) * split_pages) & 63, kWave),
+                         vpages(s), k_cache, v_cache, hkv, g, ln);
+    };
+
+    load(s0);
+    for (int i = threadIdx.x; i < 16 * D / 8; i += WAVES * 64) {
+        const int h = i / (D / 8), c = i % (D / 8);
+        *reinterpret_cast<uint4 *>(&q_lds[h][8 * c]) =
+            h < G ? *reinterpret_cast<const uint4 *>(q + r * q_row_stride + (int64_t)(g * G + h) * D + 8 * c)
+                  : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();  // q_lds ready
+
+    static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+    constexpr int EPT = D / 32;
+    const int h = threadIdx.x >> 5;  // combining thread: head h, elements dq .. dq + EPT - 1
+    const int dq = (threadIdx.x & 31) * EPT;
+    float Mg = -INFINITY, lg = 0.f, og[EPT];  // the group's fold so far
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+        og[e] = 0.f;
+    for (int s = s0; s < s1; ++s) {
+        const int buf = (s - s0) & 1;
+        const int t0 = s * S, t1 = min(t0 + S, L);
+        const int vp = vpages(s);
+        float m_run = -INFINITY, l_run = 0.f;
+        f32x4_t acc[P::DB];
+#pragma unroll
+        for (int db = 0; db < P::DB; ++db)
+            acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (wave < (vp + 1) / 2) {
+            const int keep = run_keep(wave, t0, t1, vp, ln);
+            const bool full = pair_full(wave, t0, t1);
+            if (!full)
+                mask_runs<D>(f.v, keep, f.v);
+            pair_update<D, true>(f, f.v, keep, full, &q_lds[0][0], scale_log2, ln, m_run, l_run,
+                                 acc);
+        }
+        if (s + 1 < s1)
+            load(s + 1);
+        stash_wave<D>(m_run, l_run, acc, wave, ln, c_m[buf], c_l[buf], c_acc[buf]);
+        // the split's stash complete; every combine of split s - 1 (which read the
+        // other buffer) done before split s + 1 writes it
+        __syncthreads();
+        float Ms, ls, cw[WAVES];
+        combine_ml<D>(c_m[buf], c_l[buf], h, Ms, ls, cw);
+        if (h < G) {
+            float os[EPT];
+            combine_acc<D, EPT>(c_acc[buf], cw, h, dq, os);
+            const float Mn = fmaxf(Mg, Ms);
+            const float al = exp2_hw(Mg - Mn), be = exp2_hw(Ms - Mn);
+            lg = fold_step(lg, al, be, ls);
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                og[e] = fold_step(og[e], al, be, os[e]);
+            Mg = Mn;
+        }
+    }
+    if (h < G)
+        store_partial<D, EPT>(ws + part_off(r, g, grp, h, hkv, ngmax, G, IST<D>), dq, og, Mg, lg);
+}
+
+// One wave per (row, query head): the ascending fold of the row's partials, each
+// covering S tokens (a group of splits, or one long split).  The running maxima (prefix maxima over the splits, exact, so
 // order-free) and the factors al, be of each split are formed lane-parallel,
 // one split per lane; the fold itself runs in ascending split order in every
 // lane.  Row r's length is kv_lens[r], or start + r + 1 when kv_lens is null
@@ -576,24 +692,26 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
 // token t with causal length L_t = start + t + 1, over one block-table row.
 // Each (token, query head) goes through exactly the decode arithmetic above --
 // the same split boundaries, the same page pairs per wave, the same wave
-// combine and the same ascending fold -- so its bits are those of the decode
-// row with that query and length.  What changes is the schedule: a workgroup
-// takes TG consecutive tokens of one kv head, loads each page pair of a split
-// once into its waves' registers and runs every token of the block against it.
+// combine, the same fold of each group of GROUP splits and the same ascending
+// fold of the groups -- so its bits are those of the decode row with that query
+// and length.  What changes is the schedule: a workgroup takes TG consecutive
+// tokens of one kv head, loads each page pair of a split once into its waves'
+// registers and runs every token of the block against it.
 //   FUSED:  grid (token blocks, kv heads); the workgroup walks the splits in
-//           ascending order and folds each token's split partials as they are
-//           formed, in the registers of the combining threads; no workspace.
-//   !FUSED: grid (splits, kv heads, token blocks); each workgroup writes its
-//           tokens' partials of one split to the workspace (item layout of the
-//           decode kernel) and the merge kernel folds them.  For short chunks
-//           after a long prefix, where token blocks alone cannot fill the chip.
+//           ascending order, folds each token's split partials into its group
+//           and each finished group into its total, in the registers of the
+//           combining threads; no workspace.
+//   !FUSED: grid (groups, kv heads, token blocks); each workgroup writes its
+//           tokens' group partials to the workspace (slot layout of the decode
+//           kernel) and the merge kernel folds them.  For short chunks after a
+//           long prefix, where token blocks alone cannot fill the chip.
 // Split sizes up to 2 * PAGE * WAVES = 256 tokens (one page pair per wave).
 template <int D, int TG, bool FUSED>
 __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
     const uint16_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ btrow, int start, int tokens,
     int hq, int hkv, int S, float scale_log2, uint16_t *__restrict__ out, int64_t out_row_stride,
-    int nsmax, float *__restrict__ ws)
+    int npmax, float *__restrict__ ws)
 {
     using P = AttnK<D>;
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
@@ -617,8 +735,10 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
     const int Lmax = start + tok0 + tcount;  // the block's longest length
     const int split_pages = S / PAGE;
     const int row_pages = (start + tokens + PAGE - 1) / PAGE;
-    const int s_first = FUSED ? 0 : blockIdx.x;
-    const int s_end = FUSED ? (Lmax + S - 1) / S : min((int)blockIdx.x + 1, (Lmax + S - 1) / S);
+    // FUSED: every split of the block; else the splits of group blockIdx.x
+    const int s_first = FUSED ? 0 : (int)blockIdx.x * GROUP;
+    const int s_end = FUSED ? (Lmax + S - 1) / S
+                            : min(((int)blockIdx.x + 1) * GROUP, (Lmax + S - 1) / S);
     if (s_first >= s_end)
         return;
 
@@ -633,14 +753,15 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
 
     const int h = threadIdx.x >> 5;  // combining thread: head h, elements dq .. dq + EPT - 1
     const int dq = (threadIdx.x & 31) * EPT;
-    float Mt[TG], lt[TG], ot[TG][EPT];  // FUSED: each token's fold so far
+    // each token's fold of its current group of splits, and (FUSED) of its groups
+    float Mg[TG], lg[TG], og[TG][EPT], Mt[TG], lt[TG], ot[TG][EPT];
 #pragma unroll
     for (int t = 0; t < TG; ++t) {
-        Mt[t] = -INFINITY;
-        lt[t] = 0.f;
+        Mg[t] = Mt[t] = -INFINITY;
+        lg[t] = lt[t] = 0.f;
 #pragma unroll
         for (int e = 0; e < EPT; ++e)
-            ot[t][e] = 0.f;
+            og[t][e] = ot[t][e] = 0.f;
     }
 
     __syncthreads();  // q_lds staged
@@ -683,17 +804,36 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
             if (h < G) {
                 float os[EPT];
                 combine_acc<D, EPT>(c_acc[buf], cw, h, dq, os);
-                if constexpr (FUSED) {
-                    const float Mn = fmaxf(Mt[t], Ms);
-                    const float al = exp2_hw(Mt[t] - Mn), be = exp2_hw(Ms - Mn);
-                    lt[t] = fold_step(lt[t], al, be, ls);
+                // the split into the token's group, as the decode group kernel folds it
+                {
+                    const float Mn = fmaxf(Mg[t], Ms);
+                    const float al = exp2_hw(Mg[t] - Mn), be = exp2_hw(Ms - Mn);
+                    lg[t] = fold_step(lg[t], al, be, ls);
 #pragma unroll
                     for (int e = 0; e < EPT; ++e)
-                        ot[t][e] = fold_step(ot[t][e], al, be, os[e]);
-                    Mt[t] = Mn;
-                } else {
-                    store_partial<D, EPT>(
-                        ws + part_off(tok0 + t, g, s, h, hkv, nsmax, G, IST<D>), dq, os, Ms, ls);
+                        og[t][e] = fold_step(og[t][e], al, be, os[e]);
+                    Mg[t] = Mn;
+                }
+                // the token's group ends here: at a group boundary or its last split
+                if (s % GROUP == GROUP - 1 || t0 + S >= Lt) {
+                    if constexpr (FUSED) {  // the group into the token's total, as the merge does
+                        const float Mn = fmaxf(Mt[t], Mg[t]);
+                        const float al = exp2_hw(Mt[t] - Mn), be = exp2_hw(Mg[t] - Mn);
+                        lt[t] = fold_step(lt[t], al, be, lg[t]);
+#pragma unroll
+                        for (int e = 0; e < EPT; ++e)
+                            ot[t][e] = fold_step(ot[t][e], al, be, og[t][e]);
+                        Mt[t] = Mn;
+                    } else {
+                        store_partial<D, EPT>(
+                            ws + part_off(tok0 + t, g, s / GROUP, h, hkv, npmax, G, IST<D>), dq,
+                            og[t], Mg[t], lg[t]);
+                    }
+                    Mg[t] = -INFINITY;
+                    lg[t] = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e)
+                        og[t][e] = 0.f;
                 }
             }
             buf ^= 1;
@@ -751,14 +891,16 @@ template <int D>
 hipError_t launch_attn_d(const AttnArgs &a, hipStream_t s)
 {
     const int nsmax = (a.max_kv_len + a.split - 1) / a.split;
+    const int gs = splits_per_partial(a.split);
+    const int npmax = (nsmax + gs - 1) / gs;  // partials per (row, query head), at most
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    const dim3 g1((unsigned)(nsmax * a.hkv), 1, (unsigned)a.rows), b1(WAVES * 64);
-    if (a.split <= 2 * PAGE * WAVES)
-        attn_split_kernel<D, false><<<g1, b1, 0, s>>>(
+    const dim3 b1(WAVES * 64);
+    if (gs > 1)
+        attn_group_kernel<D><<<dim3((unsigned)(npmax * a.hkv), 1, (unsigned)a.rows), b1, 0, s>>>(
             a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table, a.bt_stride, a.kv_lens,
-            a.hq, a.hkv, a.split, a.max_kv_len, nsmax, scale_log2, a.ws);
+            a.hq, a.hkv, a.split, a.max_kv_len, npmax, scale_log2, a.ws);
     else
-        attn_split_kernel<D, true><<<g1, b1, 0, s>>>(
+        attn_split_kernel<D><<<dim3((unsigned)(nsmax * a.hkv), 1, (unsigned)a.rows), b1, 0, s>>>(
             a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table, a.bt_stride, a.kv_lens,
             a.hq, a.hkv, a.split, a.max_kv_len, nsmax, scale_log2, a.ws);
     hipError_t e = hipGetLastError();
@@ -766,8 +908,9 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t s)
         return e;
     const int64_t items = a.rows * a.hq;
     const dim3 g2((unsigned)((items + 3) / 4)), b2(256);
-    attn_merge_kernel<D><<<g2, b2, 0, s>>>(a.ws, a.kv_lens, 0, a.rows, a.hq, a.hkv, a.split,
-                                           a.max_kv_len, nsmax, a.out, a.out_row_stride);
+    attn_merge_kernel<D><<<g2, b2, 0, s>>>(a.ws, a.kv_lens, 0, a.rows, a.hq, a.hkv,
+                                           a.split * gs, a.max_kv_len, npmax, a.out,
+                                           a.out_row_stride);
     return hipGetLastError();
 }
 
@@ -792,27 +935,28 @@ hipError_t launch_prefill_d(const PrefillArgs &a, hipStream_t s)
     constexpr int TG = prefill_tg(D);
     const int nblk = (int)((a.tokens + TG - 1) / TG);
     const int nsmax = (int)((a.start + a.tokens + a.split - 1) / a.split);
+    const int npmax = (nsmax + GROUP - 1) / GROUP;  // group partials per token, at most
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const dim3 blk(WAVES * 64);
     if (prefill_fused(a.tokens, a.hkv, D)) {
         attn_prefill_kernel<D, TG, true><<<dim3((unsigned)nblk, (unsigned)a.hkv), blk, 0, s>>>(
             a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table_row, (int)a.start,
-            (int)a.tokens, a.hq, a.hkv, a.split, scale_log2, a.out, a.out_row_stride, nsmax,
+            (int)a.tokens, a.hq, a.hkv, a.split, scale_log2, a.out, a.out_row_stride, npmax,
             nullptr);
         return hipGetLastError();
     }
     attn_prefill_kernel<D, TG, false>
-        <<<dim3((unsigned)nsmax, (unsigned)a.hkv, (unsigned)nblk), blk, 0, s>>>(
+        <<<dim3((unsigned)npmax, (unsigned)a.hkv, (unsigned)nblk), blk, 0, s>>>(
             a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table_row, (int)a.start,
-            (int)a.tokens, a.hq, a.hkv, a.split, scale_log2, a.out, a.out_row_stride, nsmax,
+            (int)a.tokens, a.hq, a.hkv, a.split, scale_log2, a.out, a.out_row_stride, npmax,
             a.ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     const int64_t items = a.tokens * a.hq;
     attn_merge_kernel<D><<<dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s>>>(
-        a.ws, nullptr, (int)a.start, a.tokens, a.hq, a.hkv, a.split,
-        (int)(a.start + a.tokens), nsmax, a.out, a.out_row_stride);
+        a.ws, nullptr, (int)a.start, a.tokens, a.hq, a.hkv, a.split * GROUP,
+        (int)(a.start + a.tokens), npmax, a.out, a.out_row_stride);
     return hipGetLastError();
 }
 
@@ -821,7 +965,8 @@ hipError_t launch_prefill_d(const PrefillArgs &a, hipStream_t s)
 size_t attn_workspace_bytes(int64_t rows, int hq, int d, int max_kv_len, int split)
 {
     const int64_t nsmax = (max_kv_len + split - 1) / split;
-    return (size_t)(rows * hq * nsmax) * (size_t)(d + 4) * sizeof(float);
+    const int64_t gs = splits_per_partial(split);
+    return (size_t)(rows * hq * ((nsmax + gs - 1) / gs)) * (size_t)(d + 4) * sizeof(float);
 }
 
 hipError_t launch_decode_attn(const AttnArgs &a, hipStream_t s)
@@ -834,7 +979,7 @@ size_t prefill_workspace_bytes(int64_t tokens, int hq, int hkv, int d, int64_t s
     if (prefill_fused(tokens, hkv, d))
         return 0;
     const int64_t nsmax = (start + tokens + split - 1) / split;
-    return (size_t)(tokens * hq * nsmax) * (size_t)(d + 4) * sizeof(float);
+    return (size_t)(tokens * hq * ((nsmax + GROUP - 1) / GROUP)) * (size_t)(d + 4) * sizeof(float);
 }
 
 hipError_t launch_prefill_attn(const PrefillArgs &a, hipStream_t s)

@@ -65,7 +65,7 @@ struct AttnArgs {
     int64_t rows;
     int hq, hkv, d, page, split, max_kv_len;
     float scale;
-    float *ws;  // partials: [rows, hkv, nsplit_max, hq / hkv] x (D + 4) floats
+    float *ws;  // group partials: [rows, hkv, groups_max, hq / hkv] x (D + 4) floats
 };
 size_t attn_workspace_bytes(int64_t rows, int hq, int d, int max_kv_len, int split);
 hipError_t launch_decode_attn(const AttnArgs &a, hipStream_t s);
@@ -79,7 +79,7 @@ struct PrefillArgs {
     int64_t out_row_stride;
     int hq, hkv, d, page, split;
     float scale;
-    float *ws;  // split schedule only: [tokens, hkv, nsplit_max, hq / hkv] x (D + 4) floats
+    float *ws;  // split schedule only: [tokens, hkv, groups_max, hq / hkv] x (D + 4) floats
 };
 size_t prefill_workspace_bytes(int64_t tokens, int hq, int hkv, int d, int64_t start, int split);
 hipError_t launch_prefill_attn(const PrefillArgs &a, hipStream_t s);

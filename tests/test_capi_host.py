@@ -118,20 +118,21 @@ def test_decode_attn_validation():
     assert _attn(qs=64 * 128 - 8) == EINVAL
     assert _attn(ws=NULL) == EWORKSPACE
     need = rbi.decode_attn_workspace_size(4, 64, 128, 32768, 256)
-    assert need == 4 * 64 * 128 * 132 * 4     # 128 splits of 256, 132-float slots
+    assert need == 4 * 64 * 32 * 132 * 4      # 128 splits of 256 in 32 groups, 132-float slots
     assert _attn(wsb=need - 1) == EWORKSPACE
     # grid bounds: rows <= 65535 and (splits per row) * kv heads < 2^31
     assert _attn(rows=65536) == EUNSUPPORTED
     big = dict(maxlen=(1 << 31) - 1, split=16, bts=1 << 27)   # 2^27 splits per row
     assert _attn(hq=16, hkv=16, **big) == EUNSUPPORTED
-    assert _attn(hq=16, hkv=8, **big) == EWORKSPACE           # 2^30 grid columns: in bounds
+    assert _attn(hq=16, hkv=8, wsb=1 << 20, **big) == EWORKSPACE  # 2^30 grid columns: in bounds
 
 
 def test_decode_attn_workspace_depends_only_on_bounds():
     a = rbi.decode_attn_workspace_size(256, 64, 128, 32768, 256)
-    assert a == 256 * 64 * 128 * (128 + 4) * 4
-    assert rbi.decode_attn_workspace_size(5, 4, 64, 63, 16) == 5 * 4 * 4 * 68 * 4
-    assert rbi.decode_attn_workspace_size(5, 4, 64, 65, 16) == 5 * 4 * 5 * 68 * 4
+    assert a == 256 * 64 * 32 * (128 + 4) * 4            # groups of 4 splits of 256
+    assert rbi.decode_attn_workspace_size(5, 4, 64, 63, 16) == 5 * 4 * 1 * 68 * 4
+    assert rbi.decode_attn_workspace_size(5, 4, 64, 65, 16) == 5 * 4 * 2 * 68 * 4
+    assert rbi.decode_attn_workspace_size(5, 4, 64, 4096, 512) == 5 * 4 * 8 * 68 * 4  # no groups
 
 
 def test_tuned_split_size_follows_the_batch():
@@ -196,7 +197,7 @@ def test_prefill_attn_validation():
     assert _prefill(start=1 << 30) == EUNSUPPORTED
     # a short chunk after a long prefix runs the split schedule and needs a workspace
     need = rbi.prefill_attn_workspace_size(40, 64, 4, 128, 1000, 256)
-    assert need == 40 * 64 * 5 * 132 * 4     # ceil(1040 / 256) = 5 splits
+    assert need == 40 * 64 * 2 * 132 * 4     # ceil(1040 / 256) = 5 splits in 2 groups
     assert _prefill(tokens=40, start=1000) == EWORKSPACE
     assert _prefill(tokens=40, start=1000, ws=FAKE, wsb=need - 1) == EWORKSPACE
 

@@ -166,7 +166,8 @@ def test_grid_extent_and_page_placement_do_not_matter():
 def test_kv_growth_across_split_boundaries():
     # one request grows by one token per step from 240 to 2100 tokens, crossing the
     # split boundaries 256, 512, ..., 2048; at every length its output in a random
-    # batch equals its output alone, and the partials of completed splits never change
+    # batch equals its output alone, and the workspace partials of completed groups
+    # of four splits (1024 tokens) never change
     D, HKV, HQ, S, LMAX = 128, 4, 64, 256, 4096
     pool_lens = synth.uniform_lengths(32, 1, LMAX, seed=77)
     others = synth.paged_kv(pool_lens, HKV, D, 16, seed=7)
@@ -185,16 +186,17 @@ def test_kv_growth_across_split_boundaries():
     bt_pp[:, : bt_p.shape[1]] = bt_p
     bt_pp_d = bt_pp.to(DEV)
     rng = np.random.default_rng(12)
-    nsmax = -(-LMAX // S)
+    GS = 4                              # splits per workspace partial
+    npmax = -(-LMAX // (S * GS))
     ws1 = torch.zeros(rbi.decode_attn_workspace_size(1, HQ, D, LMAX, S), dtype=torch.uint8,
                       device=DEV)
     done = {}
     for L in range(240, 2101):
         lens1 = torch.tensor([L], dtype=torch.int32, device=DEV)
         alone = rbi.decode_attn_bi(q, kc, vc, bt_pp_d, lens1, LMAX, S, workspace=ws1)
-        # the row's partials: [kv head, split, query head of the group, acc | m | l | pad]
-        slots = ws1.view(torch.float32).view(HKV, nsmax, HQ // HKV, D + 4)
-        for k in range(L // S):
+        # the row's partials: [kv head, group, query head of the kv group, acc | m | l | pad]
+        slots = ws1.view(torch.float32).view(HKV, npmax, HQ // HKV, D + 4)
+        for k in range(L // (S * GS)):
             if k in done:
                 assert torch.equal(slots[:, k], done[k]), (L, k)
             else:
@@ -208,7 +210,7 @@ def test_kv_growth_across_split_boundaries():
                           [pool_lens[i] for i in mem[pos:]], dtype=torch.int32, device=DEV)
         ob = rbi.decode_attn_bi(qb, kc, vc, btb, lb, LMAX, S)
         assert torch.equal(ob[pos], alone[0]), L
-    assert sorted(done) == list(range(8))
+    assert sorted(done) == list(range(2))
 
 
 def test_chunked_prefill_equals_unchunked():

@@ -23,8 +23,8 @@ def _case(lens, hq, hkv, d, lmax, seed):
 
 
 def test_noalloc_equals_decode_attn_bi_on_two_calls():
-    # call 1: 64 requests of U{1..8192} tokens (64 x 64 heads x 32 splits x 132 floats,
-    # 69 MB of the 128 MiB scratch); call 2, smaller: 5 requests at head_dim 64 whose
+    # call 1: 64 requests of U{1..8192} tokens (64 x 64 heads x 8 groups of 4 splits x 132 floats,
+    # 17 MB of the 128 MiB scratch); call 2, smaller: 5 requests at head_dim 64 whose
     # partials overwrite only the start of what call 1 left there
     cases = [(synth.uniform_lengths(64, 1, 8192, seed=41), 64, 4, 128, 8192, 256),
              ([1, 17, 300, 1000, 2500], 32, 4, 64, 2500, 128)]
