@@ -253,12 +253,13 @@ int decode_attn_bi_noalloc(const void *q, int64_t q_row_stride, const void *k_ca
  * batch shape -- the per-batch scheduling of [P1] section 5.5 that the page
  * names as not batch-invariant: a row's split boundaries, and so its bits, move
  * with the batch.  The rule is the fastest split size measured on MI355X for
- * these kernels: 1024 tokens for batches of at most 4 rows, 512 for at most 8,
- * 256 above (capped near max_kv_len) -- from 9 rows on it coincides with the
- * fixed size of decode_attn_bi's usual configuration.  decode_attn_tuned_split_size() returns the size it will use;
- * kv_lens_host (optional, may be NULL) is accepted for API symmetry.  The
- * workspace is sized with decode_attn_workspace_size(..., that split size).
- * Other arguments as decode_attn_bi.
+ * these kernels: 512 tokens when 256-token splits would give fewer than two
+ * (split, kv head) work units per compute unit (counted from kv_lens_host, the
+ * lengths on the host, when given, else estimated from rows and max_kv_len), 256
+ * otherwise (capped near max_kv_len) -- so from a few rows on it coincides with
+ * decode_attn_bi's usual configuration.  decode_attn_tuned_split_size() returns
+ * the size it will use; the workspace is sized with decode_attn_workspace_size(...,
+ * that split size).  Other arguments as decode_attn_bi.
  */
 int decode_attn_tuned_split_size(int64_t rows, int num_kv_heads, int max_kv_len,
                                  const int32_t *kv_lens_host);

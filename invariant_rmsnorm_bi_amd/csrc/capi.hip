@@ -376,21 +376,33 @@ int sample_gumbel(const float *logits, int64_t logits_row_stride, int64_t rows, 
                                               stream_of(stream)));
 }
 
-// Split size of the twin, tuned to the batch: the fastest split size measured on
-// MI355X for the kernels here (decode batches of 64 query / 4 kv heads, d128,
-// lengths up to 32768): 1024 tokens for at most 4 rows, 512 for at most 8 (few
-// rows: fewer, longer splits leave less partial traffic and keep every wave
-// busy), 256 beyond (one page pair per wave: the leanest kernel, and enough
-// workgroups).  Clamped to max_kv_len rounded up to the page.  The host lengths
-// are accepted for API symmetry; the rule does not need them.
+// Split size of the twin, tuned to the batch: the fastest size measured on MI355X
+// for these kernels (decode batches of 64 query / 4 kv heads, d128, lengths up to
+// 32768, split sizes 64 .. 1024 at batch 1 .. 256): 256-token splits from batch
+// 4 up (batch 8: 59.1 us against 60.8 at 512; batch 256: 1.78 ms against 1.85 at
+// 1024), 512-token splits when the batch is so small that 256-token splits give
+// fewer than two (split, kv head) work units per compute unit (batch 1, 23.7 k
+// tokens: 17.9 against 22.1 us) -- fewer, longer splits leave fewer partials to
+// fold.  The work units are counted from the host lengths when given, else
+// estimated as half of rows * ceil(max_kv_len / 256) per kv head.  Capped near
+// max_kv_len (rounded up to the page).
 int decode_attn_tuned_split_size(int64_t rows, int num_kv_heads, int max_kv_len,
                                  const int32_t *kv_lens_host)
 {
-    (void)num_kv_heads;
-    (void)kv_lens_host;
     if (rows <= 0 || max_kv_len <= 0)
         return 16;
-    int S = rows <= 4 ? 1024 : (rows <= 8 ? 512 : 256);
+    const int64_t hkv = num_kv_heads > 0 ? num_kv_heads : 1;
+    int64_t units = 0;
+    if (kv_lens_host) {
+        for (int64_t r = 0; r < rows; ++r) {
+            const int64_t L = kv_lens_host[r] < 1 ? 1 : (kv_lens_host[r] > max_kv_len ? max_kv_len
+                                                                                   : kv_lens_host[r]);
+            units += (L + 255) / 256 * hkv;
+        }
+    } else {
+        units = rows * (((int64_t)max_kv_len + 255) / 256) * hkv / 2;
+    }
+    int S = units < 2 * 256 ? 512 : 256;
     const int cap = (max_kv_len + 15) / 16 * 16;
     while (S > 16 && S / 2 >= cap)
         S /= 2;

@@ -138,13 +138,15 @@ def test_decode_attn_workspace_depends_only_on_bounds():
 def test_tuned_split_size_follows_the_batch():
     # the twin's split size moves with the batch (the fixed-size kernel would use
     # 256 for every batch)
-    one = rbi.decode_attn_tuned_split_size(1, 4, 32768, [32768])
+    one = rbi.decode_attn_tuned_split_size(1, 4, 32768, [20000])
     many = rbi.decode_attn_tuned_split_size(256, 4, 32768, [32768] * 256)
-    assert one == 1024 and many == 256
-    assert rbi.decode_attn_tuned_split_size(4, 4, 32768, None) == 1024
-    assert rbi.decode_attn_tuned_split_size(5, 4, 32768, None) == 512
-    assert rbi.decode_attn_tuned_split_size(8, 4, 32768, None) == 512
-    assert rbi.decode_attn_tuned_split_size(9, 4, 32768, None) == 256
+    assert one == 512 and many == 256
+    # work units of 256-token splits: 4 x 127 = 508 < 512 -> 512; 4 x 128 = 512 -> 256
+    assert rbi.decode_attn_tuned_split_size(1, 4, 32768, [127 * 256]) == 512
+    assert rbi.decode_attn_tuned_split_size(1, 4, 32768, [127 * 256 + 1]) == 256
+    assert rbi.decode_attn_tuned_split_size(3, 4, 32768, [100, 20000, 9000]) == 512
+    assert rbi.decode_attn_tuned_split_size(2, 4, 32768, None) == 256   # estimate 4 x 128
+    assert rbi.decode_attn_tuned_split_size(1, 4, 32768, None) == 512
     # capped near short maximum lengths, always a multiple of the page
     short = rbi.decode_attn_tuned_split_size(1, 4, 100, None)
     assert short % 16 == 0 and 16 <= short <= 128
