@@ -59,6 +59,8 @@ def lib():
         L.orc_decode_attn.argtypes = [p, i64, p, p, p, i64, p, p, i64, i32, i32, i32, i32, d]
         L.orc_decode_attn_split.argtypes = [p, i64, p, p, p, i64, p, p, i64, i32, i32, i32, i32,
                                              d, i64]
+        L.orc_decode_attn_split_groups.argtypes = [p, i64, p, p, p, i64, p, p, i64, i32, i32,
+                                                    i32, i32, d, i64, i64]
         L.orc_split_plan.argtypes = [i64, i64, p, i64]
         L.orc_philox4x32_10.argtypes = [p, p, p]
         L.orc_gumbel_noise.argtypes = [ctypes.c_uint64, i64, i64, p]
@@ -146,9 +148,11 @@ def matmul(A: np.ndarray, W: np.ndarray) -> np.ndarray:
 
 def decode_attn(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                 block_table: np.ndarray, kv_lens: np.ndarray, scale: float,
-                split: int | None = None) -> np.ndarray:
+                split: int | None = None, group: int = 1) -> np.ndarray:
     """Unsplit decode attention (``split=None``) or the fixed-split-size
-    evaluation with ascending log-sum-exp combine (``split=S``), fp64.
+    evaluation with log-sum-exp combine (``split=S``), fp64; with ``group=G`` the
+    splits are first combined within each group of G consecutive splits and the
+    group partials then combined.
 
     q: [rows, Hq, D] bf16 bits; k_cache: [pages, Hkv, page, D] bf16 bits (token-major
     pages); v_cache: [pages, Hkv, D, page] bf16 bits (head-dim-major pages);
@@ -170,8 +174,10 @@ def decode_attn(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
             rows, hq, hkv, d, page, float(scale))
     if split is None:
         lib().orc_decode_attn(*args)
-    else:
+    elif group == 1:
         lib().orc_decode_attn_split(*args, int(split))
+    else:
+        lib().orc_decode_attn_split_groups(*args, int(split), int(group))
     return out
 
 

@@ -222,19 +222,61 @@ int64_t orc_split_plan(int64_t L, int64_t S, int64_t *starts, int64_t cap)
 /*
  * The same decode attention evaluated split by split: for each split a
  * partial state (running max m_s, sum l_s = sum_j exp(s_j - m_s), accumulator
- * acc_s = sum_j exp(s_j - m_s) v_j), then the partials combined in ascending
- * split order with the log-sum-exp rescaling
+ * acc_s = sum_j exp(s_j - m_s) v_j), then the partials combined with the
+ * log-sum-exp rescaling
  *     M = max_s m_s,  l = sum_s e^{m_s - M} l_s,  acc = sum_s e^{m_s - M} acc_s,
  *     out = acc / l.
- * The pages name split-KV and fixed split size but do not print the combine;
- * this is its standard exact form.  Used only to check, in fp64, that splitting
- * at any fixed size reaches the unsplit result.
+ * With splits_per_group > 1 the combine has two levels: the splits of each
+ * group of that many consecutive splits (absolute: splits k*G .. k*G + G - 1)
+ * are combined into a group partial by the same rule, and the group partials
+ * are then combined by it.  The pages name split-KV and fixed split size but do
+ * not print the combine; this is its standard exact form.  Used only to check,
+ * in fp64, that splitting at any fixed size, and grouping the splits, reaches
+ * the unsplit result.
  */
+static void lse_combine(const double *ms, const double *ls, const double *acc, int64_t n, int d,
+                        double *M_out, double *l_out, double *acc_out)
+{
+    double M = -INFINITY;
+    for (int64_t s = 0; s < n; ++s)
+        if (ms[s] > M)
+            M = ms[s];
+    double l = 0.0;
+    for (int i = 0; i < d; ++i)
+        acc_out[i] = 0.0;
+    for (int64_t s = 0; s < n; ++s) {
+        double c = exp(ms[s] - M);
+        l += c * ls[s];
+        for (int i = 0; i < d; ++i)
+            acc_out[i] += c * acc[s * d + i];
+    }
+    *M_out = M;
+    *l_out = l;
+}
+
+void orc_decode_attn_split_groups(const uint16_t *q, int64_t q_row_stride,
+                                  const uint16_t *k_cache, const uint16_t *v_cache,
+                                  const int32_t *block_table, int64_t bt_stride,
+                                  const int32_t *kv_lens, double *out, int64_t rows, int hq,
+                                  int hkv, int d, int page, double scale, int64_t split,
+                                  int64_t splits_per_group);
+
 void orc_decode_attn_split(const uint16_t *q, int64_t q_row_stride,
                            const uint16_t *k_cache, const uint16_t *v_cache,
                            const int32_t *block_table, int64_t bt_stride, const int32_t *kv_lens,
                            double *out, int64_t rows, int hq, int hkv, int d, int page,
                            double scale, int64_t split)
+{
+    orc_decode_attn_split_groups(q, q_row_stride, k_cache, v_cache, block_table, bt_stride,
+                                 kv_lens, out, rows, hq, hkv, d, page, scale, split, 1);
+}
+
+void orc_decode_attn_split_groups(const uint16_t *q, int64_t q_row_stride,
+                                  const uint16_t *k_cache, const uint16_t *v_cache,
+                                  const int32_t *block_table, int64_t bt_stride,
+                                  const int32_t *kv_lens, double *out, int64_t rows, int hq,
+                                  int hkv, int d, int page, double scale, int64_t split,
+                                  int64_t splits_per_group)
 {
     int group = hq / hkv;
     #pragma omp parallel for collapse(2) schedule(dynamic, 1)
@@ -273,22 +315,25 @@ void orc_decode_attn_split(const uint16_t *q, int64_t q_row_stride,
                 ms[sidx] = m;
                 ls[sidx] = l;
             }
-            double M = -INFINITY;
-            for (int64_t sidx = 0; sidx < n; ++sidx)
-                if (ms[sidx] > M)
-                    M = ms[sidx];
-            double l = 0.0;
-            double *o = out + (r * hq + h) * (int64_t)d;
-            for (int i = 0; i < d; ++i)
-                o[i] = 0.0;
-            for (int64_t sidx = 0; sidx < n; ++sidx) {
-                double c = exp(ms[sidx] - M);
-                l += c * ls[sidx];
-                for (int i = 0; i < d; ++i)
-                    o[i] += c * acc[sidx * d + i];
+            /* each group of splits_per_group consecutive splits into one partial,
+               then the groups */
+            const int64_t G = splits_per_group;
+            int64_t ng = (n + G - 1) / G;
+            double *gm = (double *)malloc(sizeof(double) * (size_t)ng);
+            double *gl = (double *)malloc(sizeof(double) * (size_t)ng);
+            double *gacc = (double *)malloc(sizeof(double) * (size_t)(ng * d));
+            for (int64_t k = 0; k < ng; ++k) {
+                int64_t s0 = k * G, cnt = n - s0 < G ? n - s0 : G;
+                lse_combine(ms + s0, ls + s0, acc + s0 * d, cnt, d, &gm[k], &gl[k], gacc + k * d);
             }
+            double M, l;
+            double *o = out + (r * hq + h) * (int64_t)d;
+            lse_combine(gm, gl, gacc, ng, d, &M, &l, o);
             for (int i = 0; i < d; ++i)
                 o[i] /= l;
+            free(gm);
+            free(gl);
+            free(gacc);
             free(ms);
             free(ls);
             free(acc);

@@ -244,10 +244,10 @@ def _kv(lens, hkv=2, d=16, page=4, seed=0):
     return synth.paged_kv(lens, hkv, d, page, seed=seed)
 
 
-def _attn(q, kv, scale, split=None):
+def _attn(q, kv, scale, split=None, group=1):
     return oracle.decode_attn(synth.bf16_bits(q), synth.bf16_bits(kv.k_cache),
                               synth.bf16_bits(kv.v_cache), kv.block_table.numpy(),
-                              kv.kv_lens.numpy(), scale, split=split)
+                              kv.kv_lens.numpy(), scale, split=split, group=group)
 
 
 def _gather(kv, r):
@@ -368,6 +368,23 @@ def test_split_merge_equals_unsplit(S):
     full = _attn(q, kv, 0.25)
     split = _attn(q, kv, 0.25, split=S)
     assert np.abs(split - full).max() <= 1e-12 * np.abs(full).max()
+
+
+@pytest.mark.parametrize("S,G", [(16, 2), (16, 4), (64, 4), (256, 4), (7, 3), (16, 64)])
+def test_grouped_split_merge_equals_unsplit(S, G):
+    # the two-level combine the GPU kernels use (splits folded within fixed groups of
+    # G consecutive splits, then the groups) reaches the unsplit softmax as well;
+    # lengths end on, before and after group boundaries
+    lens = [1, 16, 17, 63, 64, 65, 300, 1000]
+    kv = _kv(lens, hkv=2, d=16, page=16)
+    q = synth.normal((len(lens), 4, 16), seed=13)
+    full = _attn(q, kv, 0.25)
+    grouped = _attn(q, kv, 0.25, split=S, group=G)
+    assert np.abs(grouped - full).max() <= 1e-12 * np.abs(full).max()
+    # the grouping only reassociates the combine: it matches the one-level split
+    # combine to the same bound
+    ref_split = _attn(q, kv, 0.25, split=S)
+    assert np.abs(grouped - ref_split).max() <= 1e-12 * np.abs(full).max()
 
 
 def test_decode_attn_ignores_stale_slots():
