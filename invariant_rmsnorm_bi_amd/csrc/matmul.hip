@@ -169,8 +169,9 @@ __global__ __launch_bounds__(256, 2) void mm_tile_kernel(
     }
 }
 
-// Pipelined tile kernel for K a multiple of 32: a TBM x TBN output tile per
-// workgroup of WM*WN waves in a WM x WN grid, each wave owning (TBM/WM) batch rows x
+// Pipelined tile kernel for K a multiple of 32 (mm_pipe64_kernel below takes over when
+// every K range is a multiple of 64, so this one serves K = 32 mod 64): a TBM x TBN
+// output tile per workgroup of WM*WN waves in a WM x WN grid, each wave owning (TBM/WM) batch rows x
 // (TBN/WN) features.  K advances one MFMA step (32 k) per stage; P stages of
 // operand tiles are in flight at once, copied from global memory straight into LDS
 // (global_load_lds_dwordx4: no register staging), so a load has P-1 stages of MFMA
@@ -400,6 +401,232 @@ hipError_t launch_pipe(const MatmulArgs &a, hipStream_t s, int splits = 1, int64
             k_split, c_split_stride);
     else
         mm_pipe_kernel<TBM, TBN, WM, WN, P, false><<<grid, block, lds, s>>>(
+            a.A, a.lda, a.W, a.ldw, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_m, tiles_n,
+            k_split, c_split_stride);
+    return hipGetLastError();
+}
+
+// Two-step stages (K a multiple of 64): the same waves, fragment reads and MFMA sequence
+// as mm_pipe_kernel, but a stage holds 64 k, so a stage row is one whole 128-byte line
+// of its operand row.  One load instruction fills 8 rows (lane l -> row l/8, slot l%8,
+// fetching the global chunk that belongs in its slot), so every line the L1 fetches from
+// L2 is used in full by one instruction; with 64-byte rows the two halves of a line were
+// fetched by different stages, too far apart for the line to stay in the L1, and each
+// line crossed from L2 twice (the L1-to-L2 read requests of the 256 x 256 tile measured
+// half as many).  P stages are resident and one barrier serves 64 k:
+//   step 2s   : read step 2s+1's fragments (stage s) while step 2s's MFMAs run;
+//   barrier   : stage s+1 has landed for every wave, and every wave has read stage s;
+//               refill stage s's buffer with stage s+P;
+//   step 2s+1 : read step 2s+2's fragments (stage s+1) while step 2s+1's MFMAs run.
+// A load thus has 2P-2 steps of MFMA work to arrive in.  Chunk c of stage row r sits in
+// slot c ^ swz8(r).  Measured on gfx950 with the LDS bank-conflict counter over every
+// swizzle that XORs the slot with a linear function of the four row bits (a one-wave
+// probe of this read pattern): a fragment read is conflict free exactly when the offsets
+// that row bits 1 and 2 contribute differ from each other and from zero in slot bits
+// 1..2 (byte-address bits 5..6); row bits 0 and 3 may contribute anything.  swz8 takes
+// 4 for row bit 1 and 2 for row bit 2.  It depends on r % 16 only, so every fragment
+// read of a wave shares one lane-dependent address part and differs by a constant.
+constexpr int SK = 64;
+
+__device__ __forceinline__ int swz8(int r)
+{
+    return ((r & 2) << 1) | ((r & 4) >> 1);
+}
+
+template <int TBM, int TBN, int WM, int WN, int P, bool OUT_BF16>
+__global__ __launch_bounds__(64 * WM * WN, 1) void mm_pipe64_kernel(
+    const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restrict__ W, int64_t ldw,
+    void *__restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n,
+    int64_t k_split, int64_t c_split_stride)
+{
+    {
+        const int64_t kb0 = (int64_t)blockIdx.y * k_split;
+        A += kb0;
+        W += kb0;
+        K = (int)((K - kb0) < k_split ? (K - kb0) : k_split);
+        C = reinterpret_cast<char *>(C) + (int64_t)blockIdx.y * c_split_stride;
+    }
+    constexpr int NW = WM * WN;
+    constexpr int WTM = TBM / WM, WTN = TBN / WN;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int ROWS = TBM + TBN;
+    constexpr int STAGE = ROWS * SK;             // bf16 elements per stage
+    constexpr int LPW = ROWS / (8 * NW);         // 8-row load instructions per wave per stage
+    constexpr int LA = TBM / (8 * NW);           // of which fill activation rows
+    static_assert(TBM % (8 * NW) == 0 && TBN % (8 * NW) == 0 && WTM % 16 == 0 && WTN % 16 == 0,
+                  "tile shape");
+    static_assert(P >= 2, "pipeline depth");
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, BIG_GROUP_M, tm, tn);
+    const int m0 = tm * TBM, n0 = tn * TBN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave % WM, wn = wave / WM;
+    const int lr = lane & 15, lq = lane >> 4;
+
+    // byte offset of this lane's 16 bytes in load instruction i of a stage, from its
+    // operand's base; rows past M or N read a valid row whose results are never stored
+    uint32_t off[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int R = (i * NW + wave) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz8(R);
+        if (i < LA)
+            off[i] = (uint32_t)(((int64_t)min(m0 + R, M - 1) * lda + 8 * c) * 2);
+        else
+            off[i] = (uint32_t)(((int64_t)min(n0 + R - TBM, N - 1) * ldw + 8 * c) * 2);
+    }
+    const char *Ab = reinterpret_cast<const char *>(A), *Wb = reinterpret_cast<const char *>(W);
+    auto issue = [&](int stage, int buf) {
+        uint16_t *base = smem_dyn + buf * STAGE;
+        const char *a = Ab + (int64_t)stage * SK * 2, *w = Wb + (int64_t)stage * SK * 2;
+#pragma unroll
+        for (int i = 0; i < LPW; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)((i < LA ? a : w) + off[i]),
+                (void __attribute__((address_space(3))) *)(base + (i * NW + wave) * 8 * SK), 16,
+                0, 0);
+    };
+    auto read_frags = [&](int buf, int sub, bf16x8_t (&fa)[FM], bf16x8_t (&fw)[FN]) {
+        const uint16_t *base = smem_dyn + buf * STAGE;
+        const int q = sub * 4 + lq;
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            const int R = TBM + wn * WTN + b * 16 + lr;
+            fw[b] = as_bf16x8(*reinterpret_cast<const uint4 *>(base + R * SK + 8 * (q ^ swz8(R))));
+        }
+#pragma unroll
+        for (int b = 0; b < FM; ++b) {
+            const int R = wm * WTM + b * 16 + lr;
+            fa[b] = as_bf16x8(*reinterpret_cast<const uint4 *>(base + R * SK + 8 * (q ^ swz8(R))));
+        }
+    };
+
+    f32x4_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // this step's MFMAs with the next step's fragment reads between them (instruction
+    // classes: 0x8 MFMA, 0x100 LDS read), so LDS latency hides under matrix work
+    auto step = [&](const bf16x8_t (&fa)[FM], const bf16x8_t (&fw)[FN]) {
+#pragma unroll
+        for (int bm = 0; bm < FM; ++bm)
+#pragma unroll
+            for (int bn = 0; bn < FN; ++bn)
+                acc[bm][bn] = mfma_16x16x32_bf16(fw[bn], fa[bm], acc[bm][bn]);
+        constexpr int NR = FM + FN, MPR = FM * FN / NR;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - NR * MPR, 0);
+    };
+
+    const int ns = K / SK;  // an empty K range leaves acc at zero
+    bf16x8_t fa0[FM], fw0[FN], fa1[FM], fw1[FN];
+    // stages 0 .. P-1 up front; stage 0 must land before the first fragment read
+#pragma unroll
+    for (int st = 0; st < P; ++st)
+        if (st < ns)
+            issue(st, st);
+    if (ns >= P)
+        wait_loads_and_barrier<(P - 1) * LPW>();
+    else
+        wait_loads_and_barrier<0>();
+    if (ns > 0)
+        read_frags(0, 0, fa0, fw0);
+    // stage s in buffer s % P.  In the steady state (stage s+P exists) stages up to
+    // s+P-1 have been issued when stage s waits for s+1, so P-2 stages may still be in
+    // flight; the last P stages wait for everything.
+    auto stage = [&](int s, int buf, bool more, bool refill, bool all) {
+        read_frags(buf, 1, fa1, fw1);
+        step(fa0, fw0);
+        if (more) {
+            if (all)
+                wait_loads_and_barrier<0>();
+            else
+                wait_loads_and_barrier<(P - 2) * LPW>();
+            if (refill)
+                issue(s + P, buf);
+            read_frags(buf + 1 == P ? 0 : buf + 1, 0, fa0, fw0);
+        }
+        step(fa1, fw1);
+    };
+    // The buffer index stays a run-time value: with constant buffers the compiler's
+    // own LDS-DMA tracking adds a wait for the loads just issued before each fragment
+    // read, which serialises the pipeline.  The waits above already order every read
+    // after the loads it depends on.
+    int s = 0, buf = 0;
+    for (; s + P < ns; ++s) {
+        stage(s, buf, true, true, false);
+        buf = buf + 1 == P ? 0 : buf + 1;
+    }
+    for (; s < ns; ++s) {
+        stage(s, buf, s + 1 < ns, false, true);
+        buf = buf + 1 == P ? 0 : buf + 1;
+    }
+
+#pragma unroll
+    for (int bm = 0; bm < FM; ++bm) {
+        const int m = m0 + wm * WTM + bm * 16 + lr;
+        if (m >= M)
+            continue;
+#pragma unroll
+        for (int bn = 0; bn < FN; ++bn) {
+            const int n = n0 + wn * WTN + bn * 16 + 4 * lq;
+            if (n >= N)
+                continue;
+            const f32x4_t v = acc[bm][bn];
+            if constexpr (OUT_BF16) {
+                uint2 o;
+                o.x = pack_bf16x2(v[0], v[1]);
+                o.y = pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(C) + (int64_t)m * ldc + n) = o;
+            } else {
+                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(C) + (int64_t)m * ldc + n) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+    }
+}
+
+// mm_pipe64_kernel serves a launch when every K range is whole 64-k stages and every
+// operand byte it reads lies within 4 GiB of its operand's base (32-bit lane offsets)
+bool pipe64_fits(const MatmulArgs &a, int splits, int64_t k_split)
+{
+    const int64_t kr = splits == 1 ? a.K : k_split;
+    if (a.K % SK != 0 || kr % SK != 0)
+        return false;
+    const int64_t lim = (int64_t)1 << 32;
+    return ((a.M - 1) * a.lda + kr) * 2 < lim && ((a.N - 1) * a.ldw + kr) * 2 < lim;
+}
+
+template <int TBM, int TBN, int WM, int WN, int P>
+hipError_t launch_pipe64(const MatmulArgs &a, hipStream_t s, int splits, int64_t k_split,
+                         int64_t c_split_stride)
+{
+    if (splits == 1)
+        k_split = a.K;
+    const int tiles_m = (int)((a.M + TBM - 1) / TBM), tiles_n = (int)((a.N + TBN - 1) / TBN);
+    const size_t lds = (size_t)P * (TBM + TBN) * SK * sizeof(uint16_t);
+    const void *fn = a.c_bf16 ? (const void *)mm_pipe64_kernel<TBM, TBN, WM, WN, P, true>
+                              : (const void *)mm_pipe64_kernel<TBM, TBN, WM, WN, P, false>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess)
+        return e;
+    const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits), block(64 * WM * WN);
+    if (a.c_bf16)
+        mm_pipe64_kernel<TBM, TBN, WM, WN, P, true><<<grid, block, lds, s>>>(
+            a.A, a.lda, a.W, a.ldw, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_m, tiles_n,
+            k_split, c_split_stride);
+    else
+        mm_pipe64_kernel<TBM, TBN, WM, WN, P, false><<<grid, block, lds, s>>>(
             a.A, a.lda, a.W, a.ldw, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_m, tiles_n,
             k_split, c_split_stride);
     return hipGetLastError();
@@ -638,16 +865,16 @@ int best_tile(int64_t M, int64_t N, double *cost)
         }
     }
     // With N <= 4096 (the long-K o_proj and down projection shapes), a single
-    // partial round of 256 x 128 tiles is slower than the four-stage 128 x 128 tile
-    // at up to two workgroups per compute unit, which the per-round pricing above
-    // does not see (graph-replayed over four operand sets, o_proj M = 1280 / 1536:
-    // 144.9 / 146.0 -> 128.4 / 123.9 us; down projection: 226.8 / 226.6 -> 201.6 /
-    // 194.0 us).  With a full round (M = 2048) or a wide N (QKV, gate/up, where the
-    // 256 x 128 tile stays ahead) the priced choice stands.
+    // partial round of 256 x 128 tiles is slower than one round of 128 x 128 tiles,
+    // which the per-round pricing above does not see (graph-replayed, o_proj M =
+    // 1024: 103.6 -> 75.6 us; down projection: 175.0 -> 122.8 us).  From 1.5 rounds
+    // of 128 x 128 tiles on, the 256 x 128 round is the faster (o_proj M = 1536: 128.6
+    // vs 106.1 us; down: 215.8 vs 176.2 us), and with a full round (M = 2048) or a
+    // wide N (QKV, gate/up) the priced choice stands.
     if (best == 1 && N <= 4096) {
         const int64_t t1 = ((M + 255) / 256) * ((N + 127) / 128);
         const int64_t t2 = ((M + 127) / 128) * ((N + 127) / 128);
-        if (t1 < 256 && t2 <= 512) {
+        if (t1 < 256 && t2 <= 256) {
             *cost = tile_cost(2, M, N);
             return 2;
         }
@@ -656,24 +883,41 @@ int best_tile(int64_t M, int64_t N, double *cost)
     return best;
 }
 
+// An LDS-pipelined tile: P64 stages of 64 k when every K range is whole 64-k stages,
+// else P32 stages of 32 k.  Both kernels give every element the same bits.
+template <int TBM, int TBN, int WM, int WN, int P64, int P32>
+hipError_t launch_lds_tile(const MatmulArgs &a, hipStream_t s, int splits, int64_t k_split,
+                           int64_t c_split_stride)
+{
+    if (pipe64_fits(a, splits, k_split))
+        return launch_pipe64<TBM, TBN, WM, WN, P64>(a, s, splits, k_split, c_split_stride);
+    return launch_pipe<TBM, TBN, WM, WN, P32>(a, s, splits, k_split, c_split_stride);
+}
+
 hipError_t launch_tile_shape(int i, const MatmulArgs &a, hipStream_t s, int splits = 1,
                              int64_t k_split = 0, int64_t c_split_stride = 0)
 {
+    // Stage counts, measured with graph-replayed device time on the decode-layer
+    // projection shapes at M = 16 .. 4096: the 64-k kernel keeps the 32-k kernel's LDS
+    // budget except for the 128-row tiles, which need three 64-k stages (two left loads
+    // too little MFMA work to arrive in: o_proj M = 512 on 128 x 64 tiles 48.7 us in
+    // 32-k stages, 59.2 in two 64-k stages, 43.9 in three; down M = 1024 on 128 x 128
+    // tiles 131.9 / 140.5 / 124.4 us).
     switch (i) {
-    case 0: return launch_pipe<256, 256, 2, 4, 4>(a, s, splits, k_split, c_split_stride);
-    case 1: return launch_pipe<256, 128, 2, 2, 6>(a, s, splits, k_split, c_split_stride);
-    // 128-row tiles with four stages: 64 or 48 KiB of LDS, two or three workgroups per
-    // compute unit (measured as fast or faster than 8 and 12 stages at every M from
-    // 48 to 4096 on the decode-layer shapes, e.g. QKV M = 4096 as one 128 x 128 launch
-    // 427 -> 358 us)
-    case 2: return launch_pipe<128, 128, 2, 2, 4>(a, s, splits, k_split, c_split_stride);
-    case 3: return launch_pipe<128, 64, 2, 2, 4>(a, s, splits, k_split, c_split_stride);
-    case 4: return launch_pipe<64, 64, 2, 2, 8>(a, s, splits, k_split, c_split_stride);
-    case 5: return launch_pipe<64, 32, 2, 1, 16>(a, s, splits, k_split, c_split_stride);
-    case 6: return launch_pipe<16, 16, 1, 1, 16>(a, s, splits, k_split, c_split_stride);
-    case 7: return launch_pipe<32, 16, 1, 1, 16>(a, s, splits, k_split, c_split_stride);
+    case 0: return launch_lds_tile<256, 256, 2, 4, 2, 4>(a, s, splits, k_split, c_split_stride);
+    case 1: return launch_lds_tile<256, 128, 2, 2, 3, 6>(a, s, splits, k_split, c_split_stride);
+    // 32-k stages: four, i.e. 64 or 48 KiB of LDS, two or three workgroups per compute
+    // unit (measured as fast or faster than 8 and 12 stages at every M from 48 to 4096
+    // on the decode-layer shapes, e.g. QKV M = 4096 as one 128 x 128 launch 427 -> 358
+    // us)
+    case 2: return launch_lds_tile<128, 128, 2, 2, 3, 4>(a, s, splits, k_split, c_split_stride);
+    case 3: return launch_lds_tile<128, 64, 2, 2, 3, 4>(a, s, splits, k_split, c_split_stride);
+    case 4: return launch_lds_tile<64, 64, 2, 2, 4, 8>(a, s, splits, k_split, c_split_stride);
+    case 5: return launch_lds_tile<64, 32, 2, 1, 8, 16>(a, s, splits, k_split, c_split_stride);
+    case 6: return launch_lds_tile<16, 16, 1, 1, 8, 16>(a, s, splits, k_split, c_split_stride);
+    case 7: return launch_lds_tile<32, 16, 1, 1, 8, 16>(a, s, splits, k_split, c_split_stride);
     case 8: return launch_stream<16, 12>(a, s, splits, k_split, c_split_stride);
-    default: return launch_pipe<32, 32, 2, 1, 16>(a, s, splits, k_split, c_split_stride);
+    default: return launch_lds_tile<32, 32, 2, 1, 8, 16>(a, s, splits, k_split, c_split_stride);
     }
 }
 

@@ -244,6 +244,16 @@ def test_exact_matmul_cases_reach_every_tile_shape():
     every = {(256, 256, 0), (256, 128, 0), (128, 128, 0), (128, 64, 0), (64, 64, 0), (64, 32, 0),
              (32, 32, 0), (32, 16, 0), (16, 16, 0), (16, 16, 1), (128, 128, 2)}
     assert seen == every, every ^ seen
+    # every LDS-pipelined shape runs in both of its kernels: 64-k stages (K % 64 == 0)
+    # and 32-k stages (K % 64 == 32)
+    lds = {t for t in every if t[2] == 0}
+    kinds = set()
+    for mnk in SMALL_EXACT_CASES + [c for c, _ in BIG_EXACT_CASES]:
+        p = rbi.matmul_bi_plan(*mnk)
+        for t in (p["first"], p["second"]):
+            if t in lds and mnk[2] % 32 == 0:
+                kinds.add((t, mnk[2] % 64))
+    assert kinds == {(t, r) for t in lds for r in (0, 32)}, {(t, r) for t in lds for r in (0, 32)} ^ kinds
     for mnk, plan in BIG_EXACT_CASES:
         p = rbi.matmul_bi_plan(*mnk)
         assert (p["first"], p["n1"], p["second"]) == plan, mnk

@@ -85,8 +85,20 @@ BIG_EXACT_CASES = [
     ((2048, 9216, 4096), ((256, 256, 0), 8192, (128, 64, 0))),    # other right-hand tile
     ((4096, 4096, 8192), ((256, 256, 0), 4096, None)),            # o_proj: one launch
     ((768, 9216, 4096), ((256, 128, 0), 9216, None)),
-    ((1280, 4096, 8192), ((128, 128, 0), 4096, None)),
+    ((1024, 4096, 8192), ((128, 128, 0), 4096, None)),
+    ((1536, 4096, 8192), ((256, 128, 0), 4096, None)),
     ((509, 4096, 8192), ((128, 64, 0), 4096, None)),
+    # K = 32 mod 64: every LDS tile shape in its 32-k-stage kernel (the shapes above
+    # run the 64-k-stage kernel)
+    ((4096, 4096, 4128), ((256, 256, 0), 4096, None)),
+    ((1536, 4096, 4128), ((256, 128, 0), 4096, None)),
+    ((600, 4096, 4128), ((128, 128, 0), 4096, None)),
+    ((300, 4096, 4128), ((128, 64, 0), 4096, None)),
+    ((130, 4096, 4128), ((64, 64, 0), 4096, None)),
+    ((65, 4096, 4128), ((64, 32, 0), 4096, None)),
+    ((33, 4096, 4128), ((32, 32, 0), 4096, None)),
+    ((17, 9216, 4128), ((32, 16, 0), 9216, None)),
+    ((17, 4096, 4128), ((16, 16, 0), 4096, None)),
 ]
 
 
