@@ -282,7 +282,7 @@ def twin_points(wl: Workload):
                     B < 1024))  # the twin's workgroup-per-row tree below 1024 rows
     for nm, A, W, C, K in (("qkv", wl.a_qkv[0], wl.w_qkv[0], wl.c_qkv, QKV[1]),
                            ("oproj", wl.a_o[0], wl.w_o[0], wl.c_o, OPROJ[1])):
-        for M in (1, 7, 64, 127, 256, 509, 1024, 2039, 4096):
+        for M in (1, 7, 64, 127, 160, 256, 509, 1024, 2039, 4096):
             ws = torch.empty(max(16, rbi.matmul_tuned_workspace_size(M, W.shape[0], K)),
                              dtype=torch.uint8, device=DEV)
             pts.append((f"matmul {nm} M={M}",

@@ -1005,18 +1005,22 @@ hipError_t launch_matmul_bi(const MatmulArgs &a, hipStream_t s)
 
 // The twin's schedule: a tile shape and a split-K count, picked from (M, N, K) by a
 // table measured on MI355X (graph-replayed device time on the decode layer's
-// projection shapes, every pipelined tile shape x splits 1, 2, 4 at M = 1 .. 4096):
-// wherever a split beat matmul_bi's own plan by a clear margin it is taken, and
-// everywhere else the twin runs matmul_bi's plan unchanged.  Winning splits:
+// projection shapes, every pipelined tile shape x 2 and 4 equal K ranges, M = 9 ..
+// 1024): wherever a split beat matmul_bi's own plan by a clear margin it is taken,
+// and everywhere else the twin runs matmul_bi's plan unchanged.  Winning splits:
 //  * long K with few output columns (N <= 4096, K >= 8192: o_proj, the down
-//    projection): from M = 9 on, K in 2 or 4 ranges (o_proj M = 64: 23.4 -> 17.3
-//    us; M = 127: 29.1 -> 21.4; M = 256: 33.6 -> 28.6; M = 509: 47.4 -> 44.0;
-//    down M = 127: 41.2 -> 27.7); at M <= 8 the register-streaming tile is faster
-//    than any split (o_proj M = 1: 11.4 vs 14.3 us), from M = 1024 no split wins;
-//  * QKV-wide N (8192 < N <= 12288, K <= 4096) at 81 <= M <= 160: 128 x 128 tiles
-//    in 2 ranges (M = 127: 27.3 -> 24.9 us);
-//  * very wide N (N >= 16384: gate/up) at M <= 16: 64 x 64 tiles in 2 ranges
-//    (M = 16: 34.9 -> 32.6 us).
+//    projection) from M = 9: 16 x 16 tiles in 2 ranges up to M = 16, 32 x 32 in 2
+//    up to 32, 64 x 64 in 4 up to 64, 128 x 64 in 4 up to 160 and in 2 up to 256
+//    (o_proj M = 16: 16.7 -> 14.8 us; M = 64: 19.9 -> 16.3; M = 127: 26.1 -> 19.0;
+//    M = 256: 29.6 -> 26.6; down M = 127: 43.1 -> 27.9; M = 256: 49.9 -> 41.7).
+//    Beyond M = 256 only the longest K gains: with K >= 12288, 256 x 128 tiles in 4
+//    ranges up to M = 512 and 256 x 256 in 4 up to 768 (down M = 509: 72.7 ->
+//    65.5 us; M = 768: 110.3 -> 91.8); o_proj there runs bi's plan (M = 384: 38.6
+//    us, no split under 38.7);
+//  * QKV-wide N (8192 < N <= 12288, K <= 4096) at 129 <= M <= 192: 64 x 64 tiles in
+//    2 ranges (M = 160: 35.4 -> 29.0 us; M = 192: 35.6 -> 30.8);
+//  * very wide N (N >= 16384: gate/up) up to M = 32: 64 x 64 tiles in 2 ranges
+//    (M = 16: 42.8 -> 37.0 us; M = 32: 44.6 -> 38.8).
 // The partition is a function of M, so the bits move with M.  With K % 32 != 0 the
 // 128 x 128 register-staged kernel splits K until its tiles fill the chip.
 TwinPlan plan_matmul_tuned(int64_t M, int64_t N, int64_t K)
@@ -1028,18 +1032,25 @@ TwinPlan plan_matmul_tuned(int64_t M, int64_t N, int64_t K)
             splits *= 2;
         return TwinPlan{-1, splits};
     }
-    if (N <= 4096 && K >= 8192 && M > 8 && M <= 768) {
+    if (N <= 4096 && K >= 8192 && M > 8) {
         if (M <= 16)
             return TwinPlan{6, 2};   // 16 x 16
+        if (M <= 32)
+            return TwinPlan{9, 2};   // 32 x 32
         if (M <= 64)
             return TwinPlan{4, 4};   // 64 x 64
         if (M <= 160)
             return TwinPlan{3, 4};   // 128 x 64
-        return TwinPlan{2, M <= 384 ? 4 : 2};  // 128 x 128
+        if (M <= 256)
+            return TwinPlan{3, 2};
+        if (K >= 12288 && M <= 512)
+            return TwinPlan{1, 4};   // 256 x 128
+        if (K >= 12288 && M <= 768)
+            return TwinPlan{0, 4};   // 256 x 256
     }
-    if (N > 8192 && N <= 12288 && K <= 4096 && M > 80 && M <= 160)
-        return TwinPlan{2, 2};
-    if (N >= 16384 && K <= 4096 && M <= 16)
+    if (N > 8192 && N <= 12288 && K <= 4096 && M > 128 && M <= 192)
+        return TwinPlan{4, 2};
+    if (N >= 16384 && K <= 4096 && M <= 32)
         return TwinPlan{4, 2};
     return TwinPlan{-1, 1};  // matmul_bi's plan
 }

@@ -77,14 +77,18 @@ def test_matmul_validation():
 
 
 def test_matmul_tuned_workspace_shape_dependence():
-    # the twin's measured table: long-K projections split K from M = 9 to 768 (4 ranges
-    # up to 384 rows, 2 beyond), QKV-wide N in 2 ranges near M = 128, very wide N in 2
-    # ranges up to M = 16; elsewhere matmul_bi's plan (no workspace, same schedule)
+    # the twin's measured table: long-K projections split K from M = 9 to 256 (and the
+    # longest K, 12288 and up, to 768), QKV-wide N in 2 ranges at M = 129 .. 192, very
+    # wide N in 2 ranges up to M = 32; elsewhere matmul_bi's plan (no workspace, same
+    # schedule)
     for M, N, K, splits in ((1, 4096, 8192, 1), (8, 4096, 8192, 1), (9, 4096, 8192, 2),
-                            (64, 4096, 8192, 4), (384, 4096, 8192, 4), (385, 4096, 8192, 2),
-                            (768, 4096, 8192, 2), (769, 4096, 8192, 1), (127, 4096, 12288, 4),
-                            (127, 9216, 4096, 2), (64, 9216, 4096, 1), (4096, 9216, 4096, 1),
-                            (16, 24576, 4096, 2), (17, 24576, 4096, 1), (1, 9216, 4096, 1)):
+                            (32, 4096, 8192, 2), (64, 4096, 8192, 4), (160, 4096, 8192, 4),
+                            (161, 4096, 8192, 2), (256, 4096, 8192, 2), (257, 4096, 8192, 1),
+                            (509, 4096, 14336, 4), (768, 4096, 14336, 4),
+                            (769, 4096, 14336, 1), (127, 4096, 12288, 4),
+                            (127, 9216, 4096, 1), (129, 9216, 4096, 2), (192, 9216, 4096, 2),
+                            (193, 9216, 4096, 1), (64, 9216, 4096, 1), (4096, 9216, 4096, 1),
+                            (32, 24576, 4096, 2), (33, 24576, 4096, 1), (1, 9216, 4096, 1)):
         assert rbi.matmul_tuned_workspace_size(M, N, K) == (splits * M * N * 4 if splits > 1
                                                             else 0), (M, N, K)
         assert rbi.matmul_tuned_differs(M, N, K) == (splits > 1), (M, N, K)
