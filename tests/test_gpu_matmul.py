@@ -124,6 +124,33 @@ def test_integer_exact_big_tiles(mnk, plan):
     assert np.array_equal(synth.bf16_bits(c16[rows]), oracle.round_bf16(ref))
 
 
+# the twin's split-K schedules (one per row of its table, plus a K = 32 mod 64 split
+# that runs its ranges in 32-k stages): (M, N, K) and the expected number of K ranges
+TWIN_EXACT_CASES = [((16, 4096, 8192), 2), ((32, 4096, 8192), 2), ((64, 4096, 8192), 4),
+                    ((127, 4096, 8192), 4), ((200, 4096, 8192), 2), ((509, 4096, 14336), 4),
+                    ((768, 4096, 14336), 4), ((160, 9216, 4096), 2), ((32, 24576, 4096), 2),
+                    ((64, 4096, 8224), 4)]
+
+
+@pytest.mark.parametrize("mnk,splits", TWIN_EXACT_CASES, ids=lambda v: str(v))
+def test_integer_exact_twin_splits(mnk, splits):
+    # integers in [-4, 4]: each K range's partial sums and their fp32 sum are exact,
+    # so the split-K twin must equal the oracle bit for bit on sampled rows (tile
+    # boundaries included), like matmul_bi
+    M, N, K = mnk
+    assert rbi.matmul_tuned_workspace_size(M, N, K) == splits * M * N * 4
+    A = synth.integer_valued((M, K), seed=5 * M + K)
+    W = synth.integer_valued((N, K), seed=N + 7)
+    Ag, Wg = A.to(DEV), W.to(DEV)
+    c32 = rbi.matmul_tuned(Ag, Wg, out_dtype=torch.float32)
+    c16 = rbi.matmul_tuned(Ag, Wg)
+    rows = sorted({0, 1, 15, 16, 63, 64, 127, 128, M // 2, M - 2, M - 1})
+    rows = [r for r in rows if r < M]
+    ref = oracle.matmul(synth.bf16_bits(A[rows]), synth.bf16_bits(W))
+    assert np.array_equal(c32[rows].double().cpu().numpy(), ref)
+    assert np.array_equal(synth.bf16_bits(c16[rows]), oracle.round_bf16(ref))
+
+
 @pytest.mark.parametrize("shape", [QKV, OPROJ])
 @pytest.mark.parametrize("M", [1, 7, 64, 127, 256])
 def test_c3_parity_normal_inputs(shape, M):
