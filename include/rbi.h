@@ -207,8 +207,8 @@ int matmul_tuned(const void *A, int64_t lda, const void *W, int64_t ldw, void *C
  *               the row's last split are not written
  * Supported: head_dim 64 or 128; page_size 16; split_size a positive multiple of
  * page_size, at most 1024; num_q_heads % num_kv_heads == 0 with a group of 1..16
- * query heads; rows <= 65535 and ceil(max_kv_len / split_size) * num_kv_heads
- * < 2^31;
+ * query heads; max_kv_len <= 2^30; rows <= 65535 and ceil(max_kv_len /
+ * split_size) * num_kv_heads < 2^31;
  * q, out 16-byte aligned with row strides multiples of 8.  A kv_lens entry
  * outside [1, max_kv_len] is clamped into that range on the device (it cannot
  * be reported from there); keep lengths valid.

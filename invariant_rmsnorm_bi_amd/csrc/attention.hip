@@ -964,7 +964,7 @@ hipError_t launch_prefill_d(const PrefillArgs &a, hipStream_t s)
 
 size_t attn_workspace_bytes(int64_t rows, int hq, int d, int max_kv_len, int split)
 {
-    const int64_t nsmax = (max_kv_len + split - 1) / split;
+    const int64_t nsmax = ((int64_t)max_kv_len + split - 1) / split;
     const int64_t gs = splits_per_partial(split);
     return (size_t)(rows * hq * ((nsmax + gs - 1) / gs)) * (size_t)(d + 4) * sizeof(float);
 }

@@ -123,7 +123,9 @@ int check_attn(const void *q, int64_t qs, const void *kc, const void *vc, const 
     if (bts < pages_needed)
         return RBI_EINVAL;
     const int64_t nsmax = ((int64_t)max_kv_len + split - 1) / split;
-    if (rows > kGridYZ || nsmax * hkv > (int64_t)0x7fffffff)
+    // lengths up to 2^30 keep every token index the kernels form (a split's end, a
+    // length rounded up to the page or split) inside int
+    if (max_kv_len > (1 << 30) || rows > kGridYZ || nsmax * hkv > (int64_t)0x7fffffff)
         return RBI_EUNSUPPORTED;
     return RBI_OK;
 }
@@ -403,7 +405,7 @@ int decode_attn_tuned_split_size(int64_t rows, int num_kv_heads, int max_kv_len,
         units = rows * (((int64_t)max_kv_len + 255) / 256) * hkv / 2;
     }
     int S = units < 2 * 256 ? 512 : 256;
-    const int cap = (max_kv_len + 15) / 16 * 16;
+    const int64_t cap = ((int64_t)max_kv_len + 15) / 16 * 16;
     while (S > 16 && S / 2 >= cap)
         S /= 2;
     return S;

@@ -124,11 +124,15 @@ def test_decode_attn_validation():
     need = rbi.decode_attn_workspace_size(4, 64, 128, 32768, 256)
     assert need == 4 * 64 * 32 * 132 * 4      # 128 splits of 256 in 32 groups, 132-float slots
     assert _attn(wsb=need - 1) == EWORKSPACE
-    # grid bounds: rows <= 65535 and (splits per row) * kv heads < 2^31
+    # bounds: lengths up to 2^30, rows <= 65535, (splits per row) * kv heads < 2^31
     assert _attn(rows=65536) == EUNSUPPORTED
-    big = dict(maxlen=(1 << 31) - 1, split=16, bts=1 << 27)   # 2^27 splits per row
-    assert _attn(hq=16, hkv=16, **big) == EUNSUPPORTED
-    assert _attn(hq=16, hkv=8, wsb=1 << 20, **big) == EWORKSPACE  # 2^30 grid columns: in bounds
+    assert _attn(maxlen=(1 << 30) + 1, bts=1 << 27) == EUNSUPPORTED
+    assert _attn(maxlen=(1 << 31) - 1, bts=1 << 27) == EUNSUPPORTED
+    big = dict(maxlen=1 << 30, split=16, bts=1 << 26)   # 2^26 splits per row
+    assert _attn(hq=32, hkv=32, **big) == EUNSUPPORTED
+    assert _attn(hq=16, hkv=16, wsb=1 << 20, **big) == EWORKSPACE  # 2^30 grid columns: in bounds
+    # the size query takes any int length without overflowing
+    assert rbi.decode_attn_workspace_size(1, 16, 64, (1 << 31) - 1, 16) == 16 * (1 << 25) * 68 * 4
 
 
 def test_decode_attn_workspace_depends_only_on_bounds():
