@@ -32,6 +32,8 @@
  *    stored as 16-bit words; every rounding to bf16 is round-to-nearest-even.
  *  - No kernel uses atomics: repeated calls on the same inputs give the same
  *    bits (run-to-run determinism, [P1] sections 4.2-4.3).
+ *  - Sizes that would need 2^31 or more threads along one grid dimension of a
+ *    launch give RBI_EUNSUPPORTED; each entry point states its bound.
  */
 #ifndef RBI_H
 #define RBI_H
@@ -85,6 +87,7 @@ const char *rbi_build_info(void);
  *  eps    added to the mean of squares, inside the root
  * Requirements: x, y, w 16-byte aligned; row strides multiples of 16 bytes
  * (8 bf16 / 4 fp32 elements) and >= hidden; hidden >= 1.  Otherwise RBI_EINVAL.
+ * rows >= 2^23 gives RBI_EUNSUPPORTED.
  */
 int rmsnorm_bi(const void *x, int64_t x_row_stride, const void *w, void *y,
                int64_t y_row_stride, int64_t rows, int64_t hidden, float eps, int dtype,
@@ -118,7 +121,7 @@ int rmsnorm_tuned(const void *x, int64_t x_row_stride, const void *w, void *y,
  * Requirements: A, W 16-byte aligned, lda and ldw multiples of 8, K a positive
  * multiple of 8, lda >= K, ldw >= K; C 16-byte aligned, ldc a multiple of 4,
  * ldc >= N, N a multiple of 4.  Otherwise RBI_EINVAL.  Sizes with
- * ceil(M/16) * ceil(N/16) >= 2^26 (more threads than one launch holds) give
+ * ceil(M/16) * ceil(N/16) >= 2^25 (the 16 x 16 tile's 64 threads each) give
  * RBI_EUNSUPPORTED.
  */
 int matmul_bi(const void *A, int64_t lda, const void *W, int64_t ldw, void *C, int64_t ldc,
@@ -207,8 +210,8 @@ int matmul_tuned(const void *A, int64_t lda, const void *W, int64_t ldw, void *C
  *               the row's last split are not written
  * Supported: head_dim 64 or 128; page_size 16; split_size a positive multiple of
  * page_size, at most 1024; num_q_heads % num_kv_heads == 0 with a group of 1..16
- * query heads; max_kv_len <= 2^30; rows <= 65535 and ceil(max_kv_len /
- * split_size) * num_kv_heads < 2^31;
+ * query heads; max_kv_len <= 2^30; rows <= 65535, rows * num_q_heads < 2^25
+ * and ceil(max_kv_len / split_size) * num_kv_heads < 2^22;
  * q, out 16-byte aligned with row strides multiples of 8.  A kv_lens entry
  * outside [1, max_kv_len] is clamped into that range on the device (it cannot
  * be reported from there); keep lengths valid.
@@ -298,8 +301,9 @@ int decode_attn_tuned(const void *q, int64_t q_row_stride, const void *k_cache,
  *                 layout with rows = tokens and max_kv_len = start_pos + tokens)
  * Supported: head_dim 64 or 128; page_size 16; split_size a positive multiple of
  * page_size, at most 256 (one page pair per wave); a group of 1..16 query heads
- * per kv head; start_pos + tokens <= 2^30; 16-byte aligned q, out and caches,
- * row strides multiples of 8.  tokens == 0 is a no-op.
+ * per kv head; start_pos + tokens <= 2^30, tokens < 2^22, tokens * num_q_heads
+ * < 2^25 and ceil((start_pos + tokens) / (4 * split_size)) < 2^22; 16-byte
+ * aligned q, out and caches, row strides multiples of 8.  tokens == 0 is a no-op.
  */
 size_t prefill_attn_workspace_size(int64_t tokens, int num_q_heads, int num_kv_heads,
                                    int head_dim, int64_t start_pos, int split_size);
@@ -353,7 +357,8 @@ int sample_gumbel(const float *logits, int64_t logits_row_stride, int64_t rows, 
  *  k_cache, v_cache  in the layouts decode_attn_bi documents (token-major K pages,
  *                head-dim-major V pages)
  * Requirements: 16-byte aligned pointers, head_dim a multiple of 8, row strides
- * multiples of 8.
+ * multiples of 8.  tokens * num_kv_heads * head_dim / 8 >= 2^31 gives
+ * RBI_EUNSUPPORTED.
  */
 int kv_append(const void *k_new, int64_t k_row_stride, const void *v_new, int64_t v_row_stride,
               const int32_t *slot_mapping, int64_t tokens, void *k_cache, void *v_cache,
@@ -364,7 +369,9 @@ int kv_append(const void *k_new, int64_t k_row_stride, const void *v_new, int64_
 /* crosses rows; [P1] section 5.4)                                             */
 /* -------------------------------------------------------------------------- */
 /* out[r,:] = table[ids[r], :]; bf16, table [vocab, hidden]; an id outside
- * [0, vocab) yields a zero row.  hidden a multiple of 8, 16-byte aligned. */
+ * [0, vocab) yields a zero row.  hidden a multiple of 8, 16-byte aligned.
+ * Each glue op runs one thread per 8 elements (argmax: a 1024-thread workgroup
+ * per row); sizes needing 2^31 threads or more give RBI_EUNSUPPORTED. */
 int rbi_embed(const void *table, int64_t vocab, int64_t hidden, const int32_t *ids, int64_t rows,
               void *out, int64_t out_row_stride, void *stream);
 
@@ -387,7 +394,8 @@ int rbi_argmax_rows(const float *x, int64_t x_row_stride, int64_t rows, int64_t 
 /* rbi_stream_copy: dst[0, bytes) = src[0, bytes), one 16-byte chunk per thread,
  * with ordinary or (nontemporal != 0) non-temporal stores: the read + write rate
  * a read-once write-once kernel such as rmsnorm_bi is judged against.  bytes a
- * multiple of 16, both pointers 16-byte aligned, the ranges must not overlap. */
+ * multiple of 16 and below 2^35, both pointers 16-byte aligned, the ranges must
+ * not overlap. */
 int rbi_stream_copy(const void *src, void *dst, int64_t bytes, int nontemporal, void *stream);
 
 #ifdef __cplusplus

@@ -55,6 +55,10 @@ inline hipStream_t stream_of(void *s)
 }
 
 constexpr int64_t kGridYZ = 65535;  // maximum grid extent in y and z
+// Every launch keeps fewer than kMaxThreadsX threads along the grid's x dimension
+// (blocks x threads per block), the range the dispatch packet's 32-bit grid size
+// holds with a margin; the checks below bound the sizes that feed each launch.
+constexpr int64_t kMaxThreadsX = (int64_t)1 << 31;
 
 int check_rmsnorm(const void *x, int64_t xs, const void *w, void *y, int64_t ys, int64_t rows,
                   int64_t hidden, int dtype)
@@ -70,7 +74,7 @@ int check_rmsnorm(const void *x, int64_t xs, const void *w, void *y, int64_t ys,
     const int64_t vec = dtype == RBI_BF16 ? 8 : 4;
     if (xs < hidden || ys < hidden || xs % vec || ys % vec)
         return RBI_EINVAL;
-    if (rows > (int64_t)0x7fffffff)
+    if (rows * 256 >= kMaxThreadsX)  // 256 threads per row beyond 1024 rows (512 below)
         return RBI_EUNSUPPORTED;
     return RBI_OK;
 }
@@ -90,9 +94,9 @@ int check_matmul(const void *A, int64_t lda, const void *W, int64_t ldw, void *C
         return RBI_EINVAL;
     if (M > (int64_t)0x3fffffff || N > (int64_t)0x3fffffff || K > (int64_t)0x3fffffff)
         return RBI_EUNSUPPORTED;
-    // grid bound: the smallest tile is 16 x 16 on one 64-lane wave, and a launch
-    // holds fewer than 2^32 threads (the tile count is also kept in an int)
-    if (((M + 15) / 16) * ((N + 15) / 16) >= ((int64_t)1 << 26))
+    // grid bound: the smallest tile is 16 x 16 on one 64-lane wave, and every other
+    // tile shape has fewer threads per output element
+    if (((M + 15) / 16) * ((N + 15) / 16) * 64 >= kMaxThreadsX)
         return RBI_EUNSUPPORTED;
     return RBI_OK;
 }
@@ -125,7 +129,8 @@ int check_attn(const void *q, int64_t qs, const void *kc, const void *vc, const 
     const int64_t nsmax = ((int64_t)max_kv_len + split - 1) / split;
     // lengths up to 2^30 keep every token index the kernels form (a split's end, a
     // length rounded up to the page or split) inside int
-    if (max_kv_len > (1 << 30) || rows > kGridYZ || nsmax * hkv > (int64_t)0x7fffffff)
+    if (max_kv_len > (1 << 30) || rows > kGridYZ || nsmax * hkv * 512 >= kMaxThreadsX ||
+        rows * hq * 64 >= kMaxThreadsX)
         return RBI_EUNSUPPORTED;
     return RBI_OK;
 }
@@ -338,7 +343,12 @@ int prefill_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, co
     if (q_row_stride < (int64_t)hq * d || out_row_stride < (int64_t)hq * d || q_row_stride % 8 ||
         out_row_stride % 8)
         return RBI_EINVAL;
-    if (start_pos + tokens > ((int64_t)1 << 30) || hkv > kGridYZ)
+    // fused: 512 threads per block of up to 8 tokens; split schedule: 512 per group of
+    // four splits, and the merge's 64 per (token, head)
+    const int64_t groups = (start_pos + tokens + 4 * (int64_t)split_size - 1) /
+                           (4 * (int64_t)split_size);
+    if (start_pos + tokens > ((int64_t)1 << 30) || hkv > kGridYZ || tokens * 512 >= kMaxThreadsX ||
+        groups * 512 >= kMaxThreadsX || tokens * hq * 64 >= kMaxThreadsX)
         return RBI_EUNSUPPORTED;
     const size_t need =
         rbi::prefill_workspace_bytes(tokens, hq, hkv, d, start_pos, split_size);
@@ -440,6 +450,8 @@ int kv_append(const void *k_new, int64_t k_row_stride, const void *v_new, int64_
     if (k_row_stride % 8 || v_row_stride % 8 || k_row_stride < (int64_t)num_kv_heads * head_dim ||
         v_row_stride < (int64_t)num_kv_heads * head_dim)
         return RBI_EINVAL;
+    if (tokens * num_kv_heads * (head_dim / 8) >= kMaxThreadsX)  // a thread per 16 bytes
+        return RBI_EUNSUPPORTED;
     return launched(rbi::launch_kv_append((const uint16_t *)k_new, k_row_stride,
                                           (const uint16_t *)v_new, v_row_stride, slot_mapping,
                                           tokens, (uint16_t *)k_cache, (uint16_t *)v_cache,
@@ -457,6 +469,8 @@ int rbi_embed(const void *table, int64_t vocab, int64_t hidden, const int32_t *i
     if (!table || !ids || !out || !aligned16(table) || !aligned16(out) ||
         out_row_stride < hidden || out_row_stride % 8)
         return RBI_EINVAL;
+    if (rows * (hidden / 8) >= kMaxThreadsX)
+        return RBI_EUNSUPPORTED;
     return launched(rbi::launch_embed((const uint16_t *)table, vocab, hidden, ids, rows,
                                       (uint16_t *)out, out_row_stride, stream_of(stream)));
 }
@@ -469,6 +483,8 @@ int rbi_residual_add(const void *a, const void *b, void *out, int64_t n, void *s
         return RBI_OK;
     if (!a || !b || !out)
         return RBI_EINVAL;
+    if ((n + 7) / 8 >= kMaxThreadsX)
+        return RBI_EUNSUPPORTED;
     return launched(rbi::launch_residual_add((const uint16_t *)a, (const uint16_t *)b,
                                              (uint16_t *)out, n, stream_of(stream)));
 }
@@ -482,6 +498,8 @@ int rbi_swiglu(const void *gu, int64_t gu_row_stride, void *out, int64_t out_row
         return RBI_OK;
     if (!gu || !out || gu_row_stride < 2 * inter || out_row_stride < inter)
         return RBI_EINVAL;
+    if (rows * ((inter + 7) / 8) >= kMaxThreadsX)
+        return RBI_EUNSUPPORTED;
     return launched(rbi::launch_swiglu((const uint16_t *)gu, gu_row_stride, (uint16_t *)out,
                                        out_row_stride, rows, inter, stream_of(stream)));
 }
@@ -495,7 +513,7 @@ int rbi_argmax_rows(const float *x, int64_t x_row_stride, int64_t rows, int64_t 
         return RBI_OK;
     if (!x || !out || x_row_stride < n)
         return RBI_EINVAL;
-    if (rows > (int64_t)0x7fffffff)
+    if (rows * 1024 >= kMaxThreadsX)  // a 1024-thread workgroup per row
         return RBI_EUNSUPPORTED;
     return launched(rbi::launch_argmax(x, x_row_stride, rows, n, out, stream_of(stream)));
 }
@@ -508,7 +526,7 @@ int rbi_stream_copy(const void *src, void *dst, int64_t bytes, int nontemporal, 
         return RBI_OK;
     if (!src || !dst || !aligned16(src) || !aligned16(dst))
         return RBI_EINVAL;
-    if (bytes / 16 > ((int64_t)1 << 32) * 255)
+    if (bytes / 16 >= kMaxThreadsX)
         return RBI_EUNSUPPORTED;
     return launched(rbi::launch_stream_copy(src, dst, bytes, nontemporal != 0, stream_of(stream)));
 }

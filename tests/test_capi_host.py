@@ -124,13 +124,17 @@ def test_decode_attn_validation():
     need = rbi.decode_attn_workspace_size(4, 64, 128, 32768, 256)
     assert need == 4 * 64 * 32 * 132 * 4      # 128 splits of 256 in 32 groups, 132-float slots
     assert _attn(wsb=need - 1) == EWORKSPACE
-    # bounds: lengths up to 2^30, rows <= 65535, (splits per row) * kv heads < 2^31
+    # bounds: lengths up to 2^30, rows <= 65535, (splits per row) * kv heads < 2^22
+    # (512 threads each), rows * query heads < 2^25 (the merge's 64 threads each)
     assert _attn(rows=65536) == EUNSUPPORTED
     assert _attn(maxlen=(1 << 30) + 1, bts=1 << 27) == EUNSUPPORTED
     assert _attn(maxlen=(1 << 31) - 1, bts=1 << 27) == EUNSUPPORTED
-    big = dict(maxlen=1 << 30, split=16, bts=1 << 26)   # 2^26 splits per row
-    assert _attn(hq=32, hkv=32, **big) == EUNSUPPORTED
-    assert _attn(hq=16, hkv=16, wsb=1 << 20, **big) == EWORKSPACE  # 2^30 grid columns: in bounds
+    big = dict(maxlen=1 << 26, split=32, bts=1 << 22)   # 2^21 splits per row
+    assert _attn(hq=32, hkv=2, **big) == EUNSUPPORTED
+    assert _attn(hq=16, hkv=1, wsb=1 << 20, **big) == EWORKSPACE  # 2^30 threads: in bounds
+    wide = dict(hq=1024, hkv=64, qs=1024 * 128, os=1024 * 128)
+    assert _attn(rows=32768, **wide) == EUNSUPPORTED
+    assert _attn(rows=32767, wsb=1 << 20, **wide) == EWORKSPACE
     # the size query takes any int length without overflowing
     assert rbi.decode_attn_workspace_size(1, 16, 64, (1 << 31) - 1, 16) == 16 * (1 << 25) * 68 * 4
 
@@ -172,6 +176,22 @@ def test_kv_append_and_glue_validation():
     assert L.rbi_swiglu(FAKE, 10, FAKE, 5, 3, 6, NULL) == EINVAL
     assert L.rbi_argmax_rows(FAKE, 10, 3, 20, FAKE, NULL) == EINVAL
     assert L.rbi_argmax_rows(NULL, 10, 3, 10, FAKE, NULL) == EINVAL
+
+
+def test_grid_thread_bounds():
+    # sizes that would put 2^31 or more threads along a grid dimension are refused
+    # before anything is launched (fake pointers: nothing here may reach a kernel)
+    L = rbi.lib()
+    for f in (L.rmsnorm_bi, L.rmsnorm_tuned):
+        assert f(FAKE, 8, FAKE, FAKE, 8, 1 << 23, 8, 1e-6, 1, NULL) == EUNSUPPORTED
+    big = 1 << 28
+    assert L.kv_append(FAKE, 512, FAKE, 512, FAKE, big, FAKE, FAKE, 10, 4, 128, 16, NULL) == EUNSUPPORTED
+    assert L.rbi_embed(FAKE, 100, 64, FAKE, big, FAKE, 64, NULL) == EUNSUPPORTED
+    assert L.rbi_residual_add(FAKE, FAKE, FAKE, 1 << 34, NULL) == EUNSUPPORTED
+    assert L.rbi_swiglu(FAKE, 128, FAKE, 64, big, 64, NULL) == EUNSUPPORTED
+    assert L.rbi_argmax_rows(FAKE, 16, 1 << 21, 16, FAKE, NULL) == EUNSUPPORTED
+    assert L.rbi_stream_copy(FAKE, FAKE, 1 << 35, 0, NULL) == EUNSUPPORTED
+    assert _prefill(tokens=1 << 22) == EUNSUPPORTED
 
 
 def test_binding_refuses_cpu_tensors():
