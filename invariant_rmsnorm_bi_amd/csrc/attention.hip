@@ -20,8 +20,9 @@
 //     past the split end; per wave a running max m and, per lane, a running sum
 //     of p = 2^(s2 - m) as the product sees it: p is split into two bf16 parts,
 //     hi = bf16(p) and lo = bf16(p - hi), so it keeps 16 significant bits;
-//   * acc[head][d] += HI . V + LO . V with the same MFMA (P operand A, V operand B;
-//     two MFMAs into one accumulator).  V pages
+//   * acc^T[d][head] += V^T . HI + V^T . LO with the same MFMA (V operand A, P
+//     operand B; two MFMAs into one accumulator), so a lane holds four consecutive
+//     d of its own head, the head of its scores.  V pages
 //     are stored head-dim-major ([d][token]), so one 16-byte load of a V page row is
 //     exactly the operand fragment (8 consecutive tokens at one d): no staging;
 //   * the eight waves' (m, l, acc) are combined in wave order 0 .. 7
@@ -61,10 +62,10 @@ constexpr int splits_per_partial(int split)
 {
     return split <= 2 * PAGE * WAVES ? GROUP : 1;
 }
-// Row padding of the LDS stash of the waves' accumulators, in floats: a wave
-// writes head 4 * lane_group + j at d = 16 * db + lane % 16, so with rows of
-// D + 4 floats the four lane groups start 16 banks apart and a write is free
-// of bank conflicts (with unpadded rows all four hit the same banks).
+// Row padding of the LDS stash of the waves' accumulators, in floats: lane l of a
+// wave writes its head l % 16 at d = 16 * db + 4 * (l / 16) .. +3 (16 bytes), so
+// with rows of D + 4 floats the heads of eight consecutive lanes start 16 bytes
+// apart modulo 128 and a write is free of bank conflicts.
 constexpr int CPAD = 4;
 // Row length of the LDS query tile, in bf16: a score MFMA reads 16 bytes of head
 // row lane % 16 per lane, so rows of D elements (a multiple of 256 bytes) put the
@@ -268,24 +269,25 @@ __device__ __forceinline__ void pair_update(const PairFrag<D> &f, const uint4 (&
     if constexpr (FRESH) {
         l_run = psum;
     } else {
-        const float alpha = exp2_hw(m_run - m_use);
+        const float alpha = exp2_hw(m_run - m_use);  // of head lr, which all of acc is
         l_run = fmaf(l_run, alpha, psum);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float aj = __shfl(alpha, 4 * ln.lg() + j, kWave);
+        for (int db = 0; db < P::DB; ++db)
 #pragma unroll
-            for (int db = 0; db < P::DB; ++db)
-                acc[db][j] *= aj;
-        }
+            for (int j = 0; j < 4; ++j)
+                acc[db][j] *= alpha;
     }
     m_run = m_new;
 
     const bf16x8_t pf = as_bf16x8(make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
     const bf16x8_t pfl = as_bf16x8(make_uint4(pl[0][0], pl[0][1], pl[1][0], pl[1][1]));
+    // V as operand A, P as operand B: acc[db][j] is d = 16 * db + 4 * lg + j of head lr.
+    // A fresh state's accumulator is +0, given to the first MFMA as a constant.
 #pragma unroll
     for (int db = 0; db < P::DB; ++db) {
-        acc[db] = mfma_16x16x32_bf16(pf, as_bf16x8(v[db]), acc[db]);
-        acc[db] = mfma_16x16x32_bf16(pfl, as_bf16x8(v[db]), acc[db]);
+        const f32x4_t c0 = FRESH ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[db];
+        acc[db] = mfma_16x16x32_bf16(as_bf16x8(v[db]), pf, c0);
+        acc[db] = mfma_16x16x32_bf16(as_bf16x8(v[db]), pfl, acc[db]);
     }
 }
 
@@ -295,26 +297,26 @@ __device__ __forceinline__ bool pair_full(int pr, int t0, int t1)
     return t0 + (2 * pr + 2) * PAGE <= t1;
 }
 
-// A wave's (m, l, acc) into the workgroup's combine buffers; l is the wave's
-// sum for head lr over the four lane groups in butterfly order.
+// A wave's (m, l, acc) into the workgroup's combine buffers ((m, l) head-major,
+// [head][wave]); l is the wave's sum for head lr over the four lane groups in
+// butterfly order.
 template <int D>
 __device__ __forceinline__ void stash_wave(float m_run, float l_run,
                                            const f32x4_t (&acc)[AttnK<D>::DB], int wave,
-                                           const PairLanes &ln, float (*c_m)[16],
-                                           float (*c_l)[16], float (*c_acc)[16][D + CPAD])
+                                           const PairLanes &ln, float (*c_m)[WAVES],
+                                           float (*c_l)[WAVES], float (*c_acc)[16][D + CPAD])
 {
     float l_w = l_run;
     l_w += __shfl_xor(l_w, 16, kWave);
     l_w += __shfl_xor(l_w, 32, kWave);
     if (ln.lg() == 0) {
-        c_m[wave][ln.lr()] = m_run;
-        c_l[wave][ln.lr()] = l_w;
+        c_m[ln.lr()][wave] = m_run;
+        c_l[ln.lr()][wave] = l_w;
     }
 #pragma unroll
     for (int db = 0; db < AttnK<D>::DB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            c_acc[wave][4 * ln.lg() + j][16 * db + ln.lr()] = acc[db][j];
+        *reinterpret_cast<float4 *>(&c_acc[wave][ln.lr()][16 * db + 4 * ln.lg()]) =
+            make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
 }
 
 // The split's partial for head h from the waves' stashes, in wave order
@@ -322,23 +324,29 @@ __device__ __forceinline__ void stash_wave(float m_run, float l_run,
 // l = fma(c_w, l_w, l) and acc = fma(c_w, acc_w, acc) over w, starting from 0,
 // for the EPT elements at dq.
 template <int D>
-__device__ __forceinline__ void combine_ml(const float (*c_m)[16], const float (*c_l)[16], int h,
-                                           float &M, float &l, float (&cw)[WAVES])
+__device__ __forceinline__ void combine_ml(const float (*c_m)[WAVES], const float (*c_l)[WAVES],
+                                           int h, float &M, float &l, float (&cw)[WAVES])
 {
-    float mw[WAVES];
+    static_assert(WAVES % 4 == 0, "whole 16-byte reads");
+    float mw[WAVES], lw[WAVES];
+#pragma unroll
+    for (int w = 0; w < WAVES; w += 4) {
+        const float4 m4 = *reinterpret_cast<const float4 *>(&c_m[h][w]);
+        const float4 l4 = *reinterpret_cast<const float4 *>(&c_l[h][w]);
+        mw[w] = m4.x, mw[w + 1] = m4.y, mw[w + 2] = m4.z, mw[w + 3] = m4.w;
+        lw[w] = l4.x, lw[w + 1] = l4.y, lw[w + 2] = l4.z, lw[w + 3] = l4.w;
+    }
     M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-        mw[w] = c_m[w][h];
+    for (int w = 0; w < WAVES; ++w)
         M = fmaxf(M, mw[w]);
-    }
 #pragma unroll
     for (int w = 0; w < WAVES; ++w)
         cw[w] = (mw[w] == -INFINITY) ? 0.f : exp2_hw(mw[w] - M);
     l = 0.f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w)
-        l = fmaf(cw[w], c_l[w][h], l);
+        l = fmaf(cw[w], lw[w], l);
 }
 
 template <int D, int EPT>
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(512, 2) void attn_split_kernel(
 {
     using P = AttnK<D>;
     __shared__ __attribute__((aligned(16))) uint16_t q_lds[16][QROW<D>];
-    __shared__ float c_m[WAVES][16], c_l[WAVES][16];
+    __shared__ __attribute__((aligned(16))) float c_m[16][WAVES], c_l[16][WAVES];
     __shared__ __attribute__((aligned(16))) float c_acc[WAVES][16][D + CPAD];
 
     // grid x = split * hkv + kv head: the kv heads of one split are dispatched
@@ -428,7 +436,7 @@ __global__ __launch_bounds__(512, 2) void attn_split_kernel(
 
     float m_run = -INFINITY;  // running max of head lr (log2 domain)
     float l_run = 0.f;        // this lane's share of the running sum for head lr
-    f32x4_t acc[P::DB];       // acc[db][j]: head 4*lg + j, d = 16*db + lr
+    f32x4_t acc[P::DB];       // acc[db][j]: d = 16*db + 4*lg + j of head lr
 #pragma unroll
     for (int db = 0; db < P::DB; ++db)
         acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -498,7 +506,7 @@ __global__ __launch_bounds__(512, 2) void attn_group_kernel(
 {
     using P = AttnK<D>;
     __shared__ __attribute__((aligned(16))) uint16_t q_lds[16][QROW<D>];
-    __shared__ float c_m[2][WAVES][16], c_l[2][WAVES][16];
+    __shared__ __attribute__((aligned(16))) float c_m[2][16][WAVES], c_l[2][16][WAVES];
     __shared__ __attribute__((aligned(16))) float c_acc[2][WAVES][16][D + CPAD];
 
     // grid x = group * hkv + kv head (the kv heads of a group back to back)
@@ -720,7 +728,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
     // other buffer may still be read by the previous token's combine, so one
     // barrier per token suffices
     __shared__ __attribute__((aligned(16))) uint16_t q_lds[TG][16][QROW<D>];
-    __shared__ float c_m[2][WAVES][16], c_l[2][WAVES][16];
+    __shared__ __attribute__((aligned(16))) float c_m[2][16][WAVES], c_l[2][16][WAVES];
     __shared__ __attribute__((aligned(16))) float c_acc[2][WAVES][16][D + CPAD];
 
     const int nblk = FUSED ? gridDim.x : gridDim.z;
