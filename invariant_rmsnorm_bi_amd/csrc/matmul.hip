@@ -497,7 +497,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void mm_pipe64_kernel(
                 (void __attribute__((address_space(3))) *)(base + (i * NW + wave) * 8 * SK), 16,
                 off[i], stage * SK * 2, 0, 0);
 #else
-        (void)base;
+        (void)base, (void)stage, (void)A, (void)W;
 #endif
     };
     auto read_frags = [&](int buf, int sub, bf16x8_t (&fa)[FM], bf16x8_t (&fw)[FN]) {
