@@ -179,6 +179,22 @@ __device__ __forceinline__ void load_pair(PairFrag<D> &f, int pr, int my_page, i
         f.v[db] = *reinterpret_cast<const uint4 *>(vp + 16 * db * PAGE);
 }
 
+// Workgroups go to the eight XCDs round robin by linear id, which for a grid of
+// (X, 1, rows) with X a multiple of 8 is x % 8.  A row's live workgroups are a
+// prefix of its x range (its splits or groups, kv heads innermost), so with an
+// unrotated x every row's prefix starts on XCD 0 and the XCDs at the start of the
+// rotation get the rows' odd remainders: with 17 groups of 4 kv heads per row,
+// XCDs 0..3 would take 9 of every 17 x 4 workgroups and XCDs 4..7 only 8.  Row r
+// starts its prefix (r * hkv) mod 8 positions further round, which spreads the
+// remainders evenly; the map is a bijection on [0, X) and only decides which
+// workgroup computes a (split or group, kv head), never its arithmetic.
+__device__ __forceinline__ int xcd_rotated_x(int hkv)
+{
+    const unsigned X = gridDim.x;
+    const unsigned rot = ((unsigned)blockIdx.z * (unsigned)hkv) & 7u;
+    return (int)((blockIdx.x + X - rot % X) % X);
+}
+
 // Live tokens of this lane group's run in page pair pr of the split [t0, t1)
 // (valid_pages = ceil((t1 - t0) / PAGE)).
 __device__ __forceinline__ int run_keep(int pr, int t0, int t1, int valid_pages,
@@ -413,7 +429,8 @@ __global__ __launch_bounds__(512, 2) void attn_split_kernel(
 
     // grid x = split * hkv + kv head: the kv heads of one split are dispatched
     // back to back, so the head slices of each K and V page are read close together
-    const int s = (int)(blockIdx.x / (unsigned)hkv), g = (int)(blockIdx.x % (unsigned)hkv);
+    const int bx = xcd_rotated_x(hkv);
+    const int s = bx / hkv, g = bx % hkv;
     const int64_t r = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const PairLanes ln(lane);
@@ -510,7 +527,8 @@ __global__ __launch_bounds__(512, 2) void attn_group_kernel(
     __shared__ __attribute__((aligned(16))) float c_acc[2][WAVES][16][D + CPAD];
 
     // grid x = group * hkv + kv head (the kv heads of a group back to back)
-    const int grp = (int)(blockIdx.x / (unsigned)hkv), g = (int)(blockIdx.x % (unsigned)hkv);
+    const int bx = xcd_rotated_x(hkv);
+    const int grp = bx / hkv, g = bx % hkv;
     const int64_t r = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const PairLanes ln(lane);
