@@ -221,36 +221,33 @@ __device__ __forceinline__ void mask_runs(const uint4 (&src)[AttnK<D>::DB], int 
 }
 
 // One page pair folded into the wave's running (m, l, acc) for the 16 query rows
-// at qt (LDS, [16][D]), with K from f and V from v (already masked by mask_runs
-// unless the pair is full).  Tokens past `keep` in a run get weight 0.
+// whose fragments qfrag(cc) gives (head lr, d = lg * DPL + 8 * cc ..), with K from
+// k and V from v (already masked by mask_runs unless the pair is full).  Tokens
+// past `keep` in a run get weight 0.
 //   scores  s2 = (K . q) * scale * log2(e), fp32, -inf when masked
 //   m_new   = max(m_run, max_j s2_j)           (per head, over the 32 tokens)
 //   e_j     = 2^(s2_j - m_new),  p_j = hi_j + lo_j with hi_j = bf16(e_j),
 //             lo_j = bf16(e_j - hi_j)
 //   l_run   = fma(l_run, 2^(m_run - m_new), sum of this lane's p_j in token order)
 //   acc     = acc * 2^(m_run - m_new) + HI . V + LO . V  (bf16 MFMA, fp32 accumulate)
+// In two parts: pair_scores (s2 and the pair's maximum) and pair_pv (the rest).
 // FRESH: the state is the initial (-inf, 0, 0), for which the rescaling is the
 // identity on zeros and is skipped (same bits).  full: every token of the pair
 // is live (keep = 8 in every run), so the score mask is all-pass and skipped.
-template <int D, bool FRESH>
-__device__ __forceinline__ void pair_update(const PairFrag<D> &f, const uint4 (&v)[AttnK<D>::DB],
-                                            int keep, bool full, const uint16_t *__restrict__ qt,
-                                            float scale_log2, const PairLanes &ln, float &m_run,
-                                            float &l_run, f32x4_t (&acc)[AttnK<D>::DB])
+template <int D, typename QFrag>
+__device__ __forceinline__ float pair_scores(const uint4 (&k)[2][AttnK<D>::KCH], int keep,
+                                             bool full, const QFrag &qfrag, float scale_log2,
+                                             float (&sv)[2][4])
 {
     using P = AttnK<D>;
     // scores: lane holds head lr, token 4b + j of its run
-    float sv[2][4];
     float mloc = -INFINITY;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int cc = 0; cc < P::KCH; ++cc) {
-            const bf16x8_t qf = as_bf16x8(
-                *reinterpret_cast<const uint4 *>(qt + ln.lr() * QROW<D> + ln.lg() * P::DPL + 8 * cc));
-            sc = mfma_16x16x32_bf16(as_bf16x8(f.k[b][cc]), qf, sc);
-        }
+        for (int cc = 0; cc < P::KCH; ++cc)
+            sc = mfma_16x16x32_bf16(as_bf16x8(k[b][cc]), qfrag(cc), sc);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float v = (full || 4 * b + j < keep) ? sc[j] * scale_log2 : -INFINITY;
@@ -260,6 +257,15 @@ __device__ __forceinline__ void pair_update(const PairFrag<D> &f, const uint4 (&
     }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+    return mloc;
+}
+
+template <int D, bool FRESH>
+__device__ __forceinline__ void pair_pv(const float (&sv)[2][4], float mloc,
+                                        const uint4 (&v)[AttnK<D>::DB], float &m_run,
+                                        float &l_run, f32x4_t (&acc)[AttnK<D>::DB])
+{
+    using P = AttnK<D>;
     const float m_new = FRESH ? mloc : fmaxf(m_run, mloc);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
 
@@ -305,6 +311,24 @@ __device__ __forceinline__ void pair_update(const PairFrag<D> &f, const uint4 (&
         acc[db] = mfma_16x16x32_bf16(as_bf16x8(v[db]), pf, c0);
         acc[db] = mfma_16x16x32_bf16(as_bf16x8(v[db]), pfl, acc[db]);
     }
+}
+
+// The decode form: K and V from the pair's registers, q rows from the LDS tile qt
+// ([16][QROW]).
+template <int D, bool FRESH>
+__device__ __forceinline__ void pair_update(const PairFrag<D> &f, const uint4 (&v)[AttnK<D>::DB],
+                                            int keep, bool full, const uint16_t *__restrict__ qt,
+                                            float scale_log2, const PairLanes &ln, float &m_run,
+                                            float &l_run, f32x4_t (&acc)[AttnK<D>::DB])
+{
+    using P = AttnK<D>;
+    const uint16_t *qrow = qt + ln.lr() * QROW<D> + ln.lg() * P::DPL;
+    float sv[2][4];
+    const float mloc = pair_scores<D>(
+        f.k, keep, full,
+        [&](int cc) { return as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 8 * cc)); },
+        scale_log2, sv);
+    pair_pv<D, FRESH>(sv, mloc, v, m_run, l_run, acc);
 }
 
 // True when page pair pr of the split [t0, t1) is live in every token.
@@ -717,22 +741,74 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
 // Prefill: one request's consecutive prompt tokens start .. start + tokens - 1,
 // token t with causal length L_t = start + t + 1, over one block-table row.
 // Each (token, query head) goes through exactly the decode arithmetic above --
-// the same split boundaries, the same page pairs per wave, the same wave
-// combine, the same fold of each group of GROUP splits and the same ascending
-// fold of the groups -- so its bits are those of the decode row with that query
-// and length.  What changes is the schedule: a workgroup takes TG consecutive
-// tokens of one kv head, loads each page pair of a split once into its waves'
-// registers and runs every token of the block against it.
-//   FUSED:  grid (token blocks, kv heads); the workgroup walks the splits in
-//           ascending order, folds each token's split partials into its group
-//           and each finished group into its total, in the registers of the
-//           combining threads; no workspace.
+// the same split boundaries, the same page pairs and per-pair step (pair_scores,
+// pair_pv), the same combine of a split's pairs in pair order, the same fold of
+// each group of GROUP splits and the same ascending fold of the groups -- so its
+// bits are those of the decode row with that query and length.  What changes is
+// the schedule: a workgroup of WAVES waves takes WAVES consecutive tokens of one
+// kv head, one token per wave, and copies each split's K and V pages into LDS once
+// (LDS DMA), from where every wave reads all of the split's page pairs for its
+// token.  A wave holds its token's whole state, so the pairs of a split are
+// combined in its registers: no stash and no barrier per token.  Per split:
+//   barrier (K pages in; every wave done with the V pages) -> the split's V pages
+//   requested -> pass 1: every pair's scores and maximum from K, kept in
+//   registers, and the split's maximum M -> barrier (V pages in; every wave done
+//   with K) -> the next split's K pages requested -> pass 2: per pair, the
+//   softmax weights and P.V from V, folded with weight 2^(m_pair - M) into the
+//   split's (l, acc) in pair order, as the decode folds its waves.
+//   FUSED:  1-D grid over (token block, kv head); the workgroup walks the splits in
+//           ascending order, folds each split into its group and each finished
+//           group into the token's total, in registers; no workspace.
 //   !FUSED: grid (groups, kv heads, token blocks); each workgroup writes its
 //           tokens' group partials to the workspace (slot layout of the decode
 //           kernel) and the merge kernel folds them.  For short chunks after a
 //           long prefix, where token blocks alone cannot fill the chip.
-// Split sizes up to 2 * PAGE * WAVES = 256 tokens (one page pair per wave).
-template <int D, int TG, bool FUSED>
+// Split sizes up to 2 * PAGE * WAVES = 256 tokens (at most WAVES page pairs).
+//
+// LDS images.  A 16-byte LDS read (ds_read_b128) serves a wave in passes of 16
+// lanes, lanes 0-7 with 16-23 and so on, over 64 four-byte banks: it is free of
+// bank conflicts when those 16 lanes read 16 distinct 16-byte positions modulo 256
+// bytes (the rule the matmul's measured fragment reads follow).  Page slot p of
+// an image holds the split's page p of the kv head.  V pages keep the cache's
+// head-dim-major layout: a V fragment read (rows d = 16 db + lr of 32 bytes, the
+// run's half) is conflict free as stored.  A K fragment read takes 16-byte chunk
+// lg * KCH + cc of token rows krow + 4 b, with rows of 2 D bytes; K row r stores
+// its chunk c at position c ^ kswz(r), which sends the row bits that vary within a
+// pass (0, 1 and 3) to distinct chunk bits other than the lane group's.  The
+// query rows (one 16 x D tile per token, row r = head) store chunk c at
+// c ^ qswz(r) for the same reason (row bits 0, 1, 2 vary within a pass).
+template <int D>
+__device__ __forceinline__ int kswz(int r)
+{
+    if constexpr (D == 128)
+        return r & 11;                        // row bits 0, 1, 3 -> chunk bits 0, 1, 3
+    else
+        return ((r >> 1) & 1) | ((r >> 1) & 4);  // row bit 0 picks the 128-byte half;
+                                                 // bits 1, 3 -> chunk bits 0, 2
+}
+
+template <int D>
+__device__ __forceinline__ int qswz(int r)
+{
+    if constexpr (D == 128)
+        return (r & 3) | ((r & 4) << 1);   // row bits 0, 1, 2 -> chunk bits 0, 1, 3
+    else
+        return ((r >> 1) & 1) | (r & 4);   // row bit 0 picks the half; 1, 2 -> 0, 2
+}
+
+// Wait for this wave's outstanding global loads (the LDS DMA) and LDS reads, then
+// meet the other waves.  s_waitcnt immediate (gfx9): vmcnt bits [3:0] and [15:14],
+// expcnt [6:4], lgkmcnt [11:8].  The empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void wait_dma_and_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(7 << 4);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int D, bool FUSED>
 __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
     const uint16_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ btrow, int start, int tokens,
@@ -741,26 +817,35 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
 {
     using P = AttnK<D>;
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-    constexpr int EPT = D / 32;
-    // the stash is double-buffered: token n stashes into buffer n % 2 while the
-    // other buffer may still be read by the previous token's combine, so one
-    // barrier per token suffices
-    __shared__ __attribute__((aligned(16))) uint16_t q_lds[TG][16][QROW<D>];
-    __shared__ __attribute__((aligned(16))) float c_m[2][16][WAVES], c_l[2][16][WAVES];
-    __shared__ __attribute__((aligned(16))) float c_acc[2][WAVES][16][D + CPAD];
+    constexpr int PG = PAGE * D;              // bf16 per page of one kv head
+    constexpr int CPR = D / 8;                // 16-byte chunks per K row or query row
+    constexpr int QPP = PG * 2 / 1024;        // 1 KiB DMA pieces per page
+    static_assert(WAVES % QPP == 0, "a wave copies the same piece of every page");
+    __shared__ __attribute__((aligned(16))) uint16_t k_img[2 * WAVES * PG];
+    __shared__ __attribute__((aligned(16))) uint16_t v_img[2 * WAVES * PG];
+    __shared__ __attribute__((aligned(16))) uint16_t q_img[WAVES][16 * D];
 
-    const int nblk = FUSED ? gridDim.x : gridDim.z;
-    // the blocks with the longest lengths (the most splits) are dispatched first
-    const int blk = nblk - 1 - (FUSED ? blockIdx.x : blockIdx.z);
-    const int g = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nblk = (tokens + WAVES - 1) / WAVES;
+    int rank, g;
+    if constexpr (FUSED) {
+        // kv heads innermost: with hkv dividing 8, the XCD of a workgroup (linear id
+        // mod 8) serves the same kv heads throughout, whose pages then share its L2
+        rank = (int)blockIdx.x / hkv;
+        g = (int)blockIdx.x % hkv;
+    } else {
+        rank = (int)blockIdx.z;
+        g = (int)blockIdx.y;
+    }
+    const int blk = nblk - 1 - rank;  // the blocks with the longest lengths first
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const PairLanes ln(lane);
     const int G = hq / hkv;
-    const int tok0 = blk * TG;
-    const int tcount = min(TG, tokens - tok0);
+    const int tok0 = blk * WAVES;
+    const int tcount = min(WAVES, tokens - tok0);
     const int Lmax = start + tok0 + tcount;  // the block's longest length
     const int split_pages = S / PAGE;
-    const int row_pages = (start + tokens + PAGE - 1) / PAGE;
+    const int last_entry = (start + tokens + PAGE - 1) / PAGE - 1;
     // FUSED: every split of the block; else the splits of group blockIdx.x
     const int s_first = FUSED ? 0 : (int)blockIdx.x * GROUP;
     const int s_end = FUSED ? (Lmax + S - 1) / S
@@ -768,118 +853,186 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
     if (s_first >= s_end)
         return;
 
-    for (int i = threadIdx.x; i < TG * 16 * D / 8; i += WAVES * 64) {
-        const int t = i / (16 * D / 8), hh = (i / (D / 8)) % 16, c = i % (D / 8);
-        *reinterpret_cast<uint4 *>(&q_lds[t][hh][8 * c]) =
-            (t < tcount && hh < G)
+    // The pages [0, np) of split s that the block needs, copied by LDS DMA: 64 lanes x
+    // 16 bytes per instruction, lane l to image bytes 16 l .. of its piece; piece
+    // i of the split goes to wave i % WAVES, which is always piece wave % QPP of a page.
+    int k_off, v_off;  // this lane's source element in that piece of a page
+    {
+        const int pos = (wave % QPP) * 64 + lane;  // 16-byte position in the page image
+        const int r = pos / CPR;
+        k_off = r * D + 8 * ((pos % CPR) ^ kswz<D>(r));
+        v_off = 8 * pos;
+    }
+    auto pages_of = [&](int s) { return (min(s * S + S, Lmax) - s * S + PAGE - 1) / PAGE; };
+    auto dma = [&](uint16_t *img, const uint16_t *__restrict__ cache, int off, int s) {
+        const int n = pages_of(s) * QPP;
+        for (int i = wave; i < n; i += WAVES) {
+            const int slot = i / QPP;
+            const int64_t phys = btrow[min(s * split_pages + slot, last_entry)];
+            const uint16_t *src = cache + (phys * hkv + g) * PG + off;
+            uint16_t *dst = img + slot * PG + (wave % QPP) * 512;
+#if defined(__HIP_DEVICE_COMPILE__)
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1))) *)src,
+                (void __attribute__((address_space(3))) *)dst, 16, 0, 0);
+#else
+            (void)src, (void)dst;
+#endif
+        }
+    };
+    dma(k_img, k_cache, k_off, s_first);
+
+    // the block's query tiles: token t's rows r = query head g * G + r (zero past G)
+    for (int i = threadIdx.x; i < WAVES * 16 * CPR; i += WAVES * 64) {
+        const int t = i / (16 * CPR), r = (i / CPR) % 16, c = i % CPR;
+        const uint4 v =
+            (t < tcount && r < G)
                 ? *reinterpret_cast<const uint4 *>(q + (int64_t)(tok0 + t) * q_row_stride +
-                                                   (int64_t)(g * G + hh) * D + 8 * c)
+                                                   (int64_t)(g * G + r) * D + 8 * c)
                 : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(&q_img[t][r * D + 8 * (c ^ qswz<D>(r))]) = v;
     }
 
-    const int h = threadIdx.x >> 5;  // combining thread: head h, elements dq .. dq + EPT - 1
-    const int dq = (threadIdx.x & 31) * EPT;
-    // each token's fold of its current group of splits, and (FUSED) of its groups
-    float Mg[TG], lg[TG], og[TG][EPT], Mt[TG], lt[TG], ot[TG][EPT];
-#pragma unroll
-    for (int t = 0; t < TG; ++t) {
-        Mg[t] = Mt[t] = -INFINITY;
-        lg[t] = lt[t] = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e)
-            og[t][e] = ot[t][e] = 0.f;
-    }
+    const bool live = wave < tcount;
+    const int Lt = start + tok0 + wave + 1;  // this wave's token's length (if live)
+    const uint16_t *qrow = &q_img[wave][ln.lr() * D];
+    const int qz = qswz<D>(ln.lr());
+    auto qfrag = [&](int cc) {
+        return as_bf16x8(
+            *reinterpret_cast<const uint4 *>(qrow + 8 * ((ln.lg() * P::KCH + cc) ^ qz)));
+    };
+    const int kz = kswz<D>(ln.krow());  // the same for token rows krow and krow + 4
+    const uint16_t *kbase = k_img + ln.kslot() * PG + ln.krow() * D;
+    const uint16_t *vbase = v_img + ln.vslot() * PG + ln.lr() * PAGE + ln.vrun();
 
-    __syncthreads();  // q_lds staged
-    int buf = 0;
+    // the token's fold of its current group of splits, and (FUSED) of its groups
+    float Mg = -INFINITY, lgr = 0.f, Mt = -INFINITY, lt = 0.f;
+    f32x4_t og[P::DB], ot[P::DB];
+#pragma unroll
+    for (int db = 0; db < P::DB; ++db)
+        og[db] = ot[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
     for (int s = s_first; s < s_end; ++s) {
         const int t0 = s * S;
-        const int vp_blk = (min(t0 + S, Lmax) - t0 + PAGE - 1) / PAGE;
-        const int my_page = btrow[min(s * split_pages + min(lane, split_pages - 1), row_pages - 1)];
-        PairFrag<D> f;
-        if (wave < (vp_blk + 1) / 2)
-            load_pair<D>(f, wave, my_page, vp_blk, k_cache, v_cache, hkv, g, ln);
+        wait_dma_and_barrier();  // K pages of s in (and the query tiles); V buffer free
+        dma(v_img, v_cache, v_off, s);
+        const bool act = live && t0 < Lt;  // wave-uniform
+        const int t1 = min(t0 + S, Lt);
+        const int vp = (t1 - t0 + PAGE - 1) / PAGE;  // the token's pages in the split
+        const int npair = act ? (vp + 1) / 2 : 0;
+        float sv[WAVES][2][4], mp[WAVES];
+        float M = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < TG; ++t) {
-            const int Lt = start + tok0 + t + 1;
-            if (t >= tcount || t0 >= Lt)  // the same for the whole workgroup
-                continue;
-            const int t1 = min(t0 + S, Lt);
-            const int vp = (t1 - t0 + PAGE - 1) / PAGE;
-            float m_run = -INFINITY, l_run = 0.f;
-            f32x4_t acc[P::DB];
+        for (int p = 0; p < WAVES; ++p) {
+            if (p < npair) {
+                uint4 kf[2][P::KCH];
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int cc = 0; cc < P::KCH; ++cc)
+                        kf[b][cc] = *reinterpret_cast<const uint4 *>(
+                            kbase + 2 * p * PG + 4 * b * D + 8 * ((ln.lg() * P::KCH + cc) ^ kz));
+                mp[p] = pair_scores<D>(kf, run_keep(p, t0, t1, vp, ln), pair_full(p, t0, t1),
+                                       qfrag, scale_log2, sv[p]);
+                M = fmaxf(M, mp[p]);
+            }
+        }
+        wait_dma_and_barrier();  // V pages of s in; K buffer free
+        if (s + 1 < s_end)
+            dma(k_img, k_cache, k_off, s + 1);
+        if (!act)
+            continue;
+
+        // the split's (l, acc): pair p's partial with weight 2^(m_p - M), in pair
+        // order, as the decode combines its waves (wave p holding pair p)
+        float l = 0.f;
+        f32x4_t a[P::DB];
+#pragma unroll
+        for (int db = 0; db < P::DB; ++db)
+            a[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < WAVES; ++p) {
+            if (p < npair) {
+                uint4 vf[P::DB];
+#pragma unroll
+                for (int db = 0; db < P::DB; ++db)
+                    vf[db] = *reinterpret_cast<const uint4 *>(vbase + 2 * p * PG + 16 * db * PAGE);
+                if (!pair_full(p, t0, t1))
+                    mask_runs<D>(vf, run_keep(p, t0, t1, vp, ln), vf);
+                float m_run = -INFINITY, l_run = 0.f;
+                f32x4_t acc[P::DB];
+                pair_pv<D, true>(sv[p], mp[p], vf, m_run, l_run, acc);
+                float l_w = l_run;
+                l_w += __shfl_xor(l_w, 16, kWave);
+                l_w += __shfl_xor(l_w, 32, kWave);
+                const float cw = (m_run == -INFINITY) ? 0.f : exp2_hw(m_run - M);
+                l = fmaf(cw, l_w, l);
+#pragma unroll
+                for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        a[db][j] = fmaf(cw, acc[db][j], a[db][j]);
+            }
+        }
+        if (npair < WAVES) {  // the decode's idle waves, each adding fma(0, +0, .)
+            l = fmaf(0.f, 0.f, l);
 #pragma unroll
             for (int db = 0; db < P::DB; ++db)
-                acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (wave < (vp + 1) / 2) {
-                const int keep = run_keep(wave, t0, t1, vp, ln);
-                if (pair_full(wave, t0, t1)) {
-                    pair_update<D, true>(f, f.v, keep, true, &q_lds[t][0][0], scale_log2, ln,
-                                         m_run, l_run, acc);
-                } else {  // a masked copy: the block's V image serves every token
-                    uint4 vm[P::DB];
-                    mask_runs<D>(f.v, keep, vm);
-                    pair_update<D, true>(f, vm, keep, false, &q_lds[t][0][0], scale_log2, ln,
-                                         m_run, l_run, acc);
-                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    a[db][j] = fmaf(0.f, 0.f, a[db][j]);
+        }
+        // the split into the token's group, as the decode group kernel folds it
+        {
+            const float Mn = fmaxf(Mg, M);
+            const float al = exp2_hw(Mg - Mn), be = exp2_hw(M - Mn);
+            lgr = fold_step(lgr, al, be, l);
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    og[db][j] = fold_step(og[db][j], al, be, a[db][j]);
+            Mg = Mn;
+        }
+        // the token's group ends here: at a group boundary or its last split
+        if (s % GROUP == GROUP - 1 || t0 + S >= Lt) {
+            if constexpr (FUSED) {  // the group into the token's total, as the merge does
+                const float Mn = fmaxf(Mt, Mg);
+                const float al = exp2_hw(Mt - Mn), be = exp2_hw(Mg - Mn);
+                lt = fold_step(lt, al, be, lgr);
+#pragma unroll
+                for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        ot[db][j] = fold_step(ot[db][j], al, be, og[db][j]);
+                Mt = Mn;
+            } else if (ln.lr() < G) {
+                float *dst = ws + part_off(tok0 + wave, g, s / GROUP, ln.lr(), hkv, npmax, G,
+                                           IST<D>);
+#pragma unroll
+                for (int db = 0; db < P::DB; ++db)
+                    *reinterpret_cast<float4 *>(dst + 16 * db + 4 * ln.lg()) =
+                        make_float4(og[db][0], og[db][1], og[db][2], og[db][3]);
+                if (ln.lg() == 0)
+                    *reinterpret_cast<float4 *>(dst + D) = make_float4(Mg, lgr, 0.f, 0.f);
             }
-            stash_wave<D>(m_run, l_run, acc, wave, ln, c_m[buf], c_l[buf], c_acc[buf]);
-            __syncthreads();  // this token's stash complete; every combine before the last done
-            float Ms, ls, cw[WAVES];
-            combine_ml<D>(c_m[buf], c_l[buf], h, Ms, ls, cw);
-            if (h < G) {
-                float os[EPT];
-                combine_acc<D, EPT>(c_acc[buf], cw, h, dq, os);
-                // the split into the token's group, as the decode group kernel folds it
-                {
-                    const float Mn = fmaxf(Mg[t], Ms);
-                    const float al = exp2_hw(Mg[t] - Mn), be = exp2_hw(Ms - Mn);
-                    lg[t] = fold_step(lg[t], al, be, ls);
+            Mg = -INFINITY;
+            lgr = 0.f;
 #pragma unroll
-                    for (int e = 0; e < EPT; ++e)
-                        og[t][e] = fold_step(og[t][e], al, be, os[e]);
-                    Mg[t] = Mn;
-                }
-                // the token's group ends here: at a group boundary or its last split
-                if (s % GROUP == GROUP - 1 || t0 + S >= Lt) {
-                    if constexpr (FUSED) {  // the group into the token's total, as the merge does
-                        const float Mn = fmaxf(Mt[t], Mg[t]);
-                        const float al = exp2_hw(Mt[t] - Mn), be = exp2_hw(Mg[t] - Mn);
-                        lt[t] = fold_step(lt[t], al, be, lg[t]);
-#pragma unroll
-                        for (int e = 0; e < EPT; ++e)
-                            ot[t][e] = fold_step(ot[t][e], al, be, og[t][e]);
-                        Mt[t] = Mn;
-                    } else {
-                        store_partial<D, EPT>(
-                            ws + part_off(tok0 + t, g, s / GROUP, h, hkv, npmax, G, IST<D>), dq,
-                            og[t], Mg[t], lg[t]);
-                    }
-                    Mg[t] = -INFINITY;
-                    lg[t] = 0.f;
-#pragma unroll
-                    for (int e = 0; e < EPT; ++e)
-                        og[t][e] = 0.f;
-                }
-            }
-            buf ^= 1;
+            for (int db = 0; db < P::DB; ++db)
+                og[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
 
     if constexpr (FUSED) {
-        if (h < G) {
+        if (live && ln.lr() < G) {
+            uint16_t *dst = out + (int64_t)(tok0 + wave) * out_row_stride +
+                            (int64_t)(g * G + ln.lr()) * D + 4 * ln.lg();
 #pragma unroll
-            for (int t = 0; t < TG; ++t) {
-                if (t < tcount) {
-                    uint16_t *dst = out + (int64_t)(tok0 + t) * out_row_stride + (int64_t)(g * G + h) * D + dq;
-                    if constexpr (EPT == 4)
-                        *reinterpret_cast<uint2 *>(dst) =
-                            make_uint2(pack_bf16x2(ot[t][0] / lt[t], ot[t][1] / lt[t]),
-                                       pack_bf16x2(ot[t][2] / lt[t], ot[t][3] / lt[t]));
-                    else
-                        *reinterpret_cast<uint32_t *>(dst) = pack_bf16x2(ot[t][0] / lt[t], ot[t][1] / lt[t]);
-                }
-            }
+            for (int db = 0; db < P::DB; ++db)
+                *reinterpret_cast<uint2 *>(dst + 16 * db) =
+                    make_uint2(pack_bf16x2(ot[db][0] / lt, ot[db][1] / lt),
+                               pack_bf16x2(ot[db][2] / lt, ot[db][3] / lt));
         }
     }
 }
@@ -940,44 +1093,31 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-// Prompt tokens per prefill workgroup: as many as fit in LDS beside the
-// double-buffered stash (at head_dim 128: 6 x 4 KiB of queries + 2 x 66 KiB).
-constexpr int prefill_tg(int d)
-{
-    return d == 128 ? 6 : 8;
-}
-
-// The fused prefill schedule needs enough token blocks to occupy the chip (one
+// The fused schedule needs enough token blocks to occupy the chip (one
 // workgroup per compute unit); short chunks use the split schedule.
 bool prefill_fused(int64_t tokens, int hkv, int d)
 {
-    const int64_t blocks = (tokens + prefill_tg(d) - 1) / prefill_tg(d);
+    (void)d;
+    const int64_t blocks = (tokens + WAVES - 1) / WAVES;
     return blocks * hkv >= 256;
 }
 
-// The token block of a workgroup: TG tokens share each split's page-pair loads.
-// At head_dim 128, six tokens while the fused launch has at least four rounds of
-// workgroups per compute unit, else four (more, lighter workgroups balance the
-// causal lengths better; the split schedule always runs four): graph-replayed,
-// 4096 tokens from 0 1062 us with six vs 1122 with four; 1024 tokens from 0 95.5
-// vs 90.9 us; 64 tokens after 8000, split schedule, 101.1 vs 76.7 us.  Only the
-// schedule changes: every token keeps its decode row's bits.
-template <int D, int TG, bool FUSED>
-hipError_t launch_prefill_tg(const PrefillArgs &a, hipStream_t s)
+template <int D, bool FUSED>
+hipError_t launch_prefill_sched(const PrefillArgs &a, hipStream_t s)
 {
-    const int nblk = (int)((a.tokens + TG - 1) / TG);
+    const int nblk = (int)((a.tokens + WAVES - 1) / WAVES);
     const int nsmax = (int)((a.start + a.tokens + a.split - 1) / a.split);
     const int npmax = (nsmax + GROUP - 1) / GROUP;  // group partials per token, at most
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const dim3 blk(WAVES * 64);
     if constexpr (FUSED) {
-        attn_prefill_kernel<D, TG, true><<<dim3((unsigned)nblk, (unsigned)a.hkv), blk, 0, s>>>(
+        attn_prefill_kernel<D, true><<<dim3((unsigned)(nblk * a.hkv)), blk, 0, s>>>(
             a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table_row, (int)a.start,
             (int)a.tokens, a.hq, a.hkv, a.split, scale_log2, a.out, a.out_row_stride, npmax,
             nullptr);
         return hipGetLastError();
     } else {
-        attn_prefill_kernel<D, TG, false>
+        attn_prefill_kernel<D, false>
             <<<dim3((unsigned)npmax, (unsigned)a.hkv, (unsigned)nblk), blk, 0, s>>>(
                 a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table_row, (int)a.start,
                 (int)a.tokens, a.hq, a.hkv, a.split, scale_log2, a.out, a.out_row_stride,
@@ -996,18 +1136,8 @@ hipError_t launch_prefill_tg(const PrefillArgs &a, hipStream_t s)
 template <int D>
 hipError_t launch_prefill_d(const PrefillArgs &a, hipStream_t s)
 {
-    constexpr int TG = prefill_tg(D);
-    if constexpr (D == 128) {
-        if (!prefill_fused(a.tokens, a.hkv, D))
-            return launch_prefill_tg<D, 4, false>(a, s);
-        if (((a.tokens + TG - 1) / TG) * a.hkv < 4 * 256)
-            return launch_prefill_tg<D, 4, true>(a, s);
-        return launch_prefill_tg<D, TG, true>(a, s);
-    } else {
-        if (!prefill_fused(a.tokens, a.hkv, D))
-            return launch_prefill_tg<D, TG, false>(a, s);
-        return launch_prefill_tg<D, TG, true>(a, s);
-    }
+    return prefill_fused(a.tokens, a.hkv, D) ? launch_prefill_sched<D, true>(a, s)
+                                             : launch_prefill_sched<D, false>(a, s);
 }
 
 }  // namespace

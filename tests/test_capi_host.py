@@ -233,10 +233,11 @@ def test_prefill_attn_validation():
 
 
 def test_prefill_workspace_follows_the_schedule():
-    # fused (no workspace) once ceil(tokens / TG) * num_kv_heads token blocks reach 256,
-    # TG = 6 tokens per workgroup at head_dim 128, 8 at head_dim 64
-    assert rbi.prefill_attn_workspace_size(384, 64, 4, 128, 0, 256) == 0
-    assert rbi.prefill_attn_workspace_size(378, 64, 4, 128, 0, 256) > 0
+    # fused (no workspace) once ceil(tokens / 8) * num_kv_heads token blocks reach 256
+    # (8 tokens per workgroup, one per wave)
+    assert rbi.prefill_attn_workspace_size(512, 64, 4, 128, 0, 256) == 0
+    assert rbi.prefill_attn_workspace_size(505, 64, 4, 128, 0, 256) == 0
+    assert rbi.prefill_attn_workspace_size(504, 64, 4, 128, 0, 256) > 0
     assert rbi.prefill_attn_workspace_size(512, 32, 4, 64, 0, 256) == 0
     assert rbi.prefill_attn_workspace_size(504, 32, 4, 64, 0, 256) > 0
     assert rbi.prefill_attn_workspace_size(2048, 8, 1, 64, 100, 16) == 0

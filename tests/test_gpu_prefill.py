@@ -62,15 +62,15 @@ class Prompt:
 
 
 CASES = [
-    # d, hq, hkv, split, start, tokens      schedule
-    (128, 64, 4, 256, 0, 700),            # fused (4-token blocks), every length 1..700
+    # d, hq, hkv, split, start, tokens      schedule (8-token blocks, one token per wave)
+    (128, 64, 4, 256, 0, 700),            # fused, every length 1..700, ragged last block
     (128, 64, 4, 256, 1000, 40),          # split: a short chunk after a long prefix
     (64, 8, 1, 16, 0, 100),               # split, one-page splits, group of 8
     (128, 16, 2, 64, 37, 333),            # split, ragged start and count
-    (64, 32, 4, 128, 5, 2049),            # fused, head_dim 64, ragged last block
+    (64, 32, 4, 128, 5, 2049),            # fused, head_dim 64, one-token last block
     (128, 4, 4, 256, 0, 1),               # one token, group of one
-    (128, 64, 8, 256, 3000, 513),         # fused (4-token blocks), group of 8, long prefix
-    (128, 64, 4, 32, 250, 2100),          # fused (6-token blocks), many splits per token
+    (128, 64, 8, 256, 3000, 513),         # fused, group of 8, long prefix
+    (128, 64, 4, 32, 250, 2100),          # fused, many splits per token
 ]
 
 
