@@ -39,6 +39,8 @@
 //
 // The twin (decode_attn_tuned) runs the same kernels with a split size picked
 // from the batch shape, which moves the split boundaries with the batch.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -220,6 +222,47 @@ __device__ __forceinline__ void mask_runs(const uint4 (&src)[AttnK<D>::DB], int 
                              src[db].w & vmask[3]);
 }
 
+// The maximum and the sum of x over the four 16-lane rows of a wave, in the
+// butterfly order (lane i with i ^ 16, then with i ^ 32); every lane ends with
+// the same value, since at each step both lanes of a pair combine the same two
+// operands (fp32 max and addition commute).  LANES: the partner values come from
+// v_permlane16_swap / v_permlane32_swap, which exchange the odd 16-lane rows of
+// one operand with the even rows of the other (the upper 32 lanes of one with
+// the lower 32 of the other), so with x in both operands a lane gets its own
+// value in one result and its partner's in the other -- no LDS round trip.
+// Otherwise the partner values come from LDS lane permutes (__shfl_xor).
+template <bool LANES>
+__device__ __forceinline__ float rows_max(float x)
+{
+    if constexpr (LANES) {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+        const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    } else {
+        x = fmaxf(x, __shfl_xor(x, 16, kWave));
+        return fmaxf(x, __shfl_xor(x, 32, kWave));
+    }
+}
+
+template <bool LANES>
+__device__ __forceinline__ float rows_sum(float x)
+{
+    if constexpr (LANES) {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+        const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    } else {
+        x += __shfl_xor(x, 16, kWave);
+        return x + __shfl_xor(x, 32, kWave);
+    }
+}
+
 // One page pair folded into the wave's running (m, l, acc) for the 16 query rows
 // whose fragments qfrag(cc) gives (head lr, d = lg * DPL + 8 * cc ..), with K from
 // k and V from v (already masked by mask_runs unless the pair is full).  Tokens
@@ -234,7 +277,7 @@ __device__ __forceinline__ void mask_runs(const uint4 (&src)[AttnK<D>::DB], int 
 // FRESH: the state is the initial (-inf, 0, 0), for which the rescaling is the
 // identity on zeros and is skipped (same bits).  full: every token of the pair
 // is live (keep = 8 in every run), so the score mask is all-pass and skipped.
-template <int D, typename QFrag>
+template <int D, bool LANES = false, typename QFrag>
 __device__ __forceinline__ float pair_scores(const uint4 (&k)[2][AttnK<D>::KCH], int keep,
                                              bool full, const QFrag &qfrag, float scale_log2,
                                              float (&sv)[2][4])
@@ -255,9 +298,7 @@ __device__ __forceinline__ float pair_scores(const uint4 (&k)[2][AttnK<D>::KCH],
             mloc = fmaxf(mloc, v);
         }
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-    return mloc;
+    return rows_max<LANES>(mloc);
 }
 
 template <int D, bool FRESH>
@@ -920,23 +961,36 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
         const int t1 = min(t0 + S, Lt);
         const int vp = (t1 - t0 + PAGE - 1) / PAGE;  // the token's pages in the split
         const int npair = act ? (vp + 1) / 2 : 0;
+        // every pair of the split live in every token (the common case): straight-line
+        // code without masks or per-pair branches, so loads and arithmetic of
+        // neighbouring pairs can overlap
+        const bool whole = act && S == 2 * PAGE * WAVES && t0 + S <= Lt;
         float sv[WAVES][2][4], mp[WAVES];
         float M = -INFINITY;
+        auto pass1 = [&](auto all_c) {
+            constexpr bool all = decltype(all_c)::value;
 #pragma unroll
-        for (int p = 0; p < WAVES; ++p) {
-            if (p < npair) {
-                uint4 kf[2][P::KCH];
+            for (int p = 0; p < WAVES; ++p) {
+                if (all || p < npair) {
+                    uint4 kf[2][P::KCH];
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+                    for (int b = 0; b < 2; ++b)
 #pragma unroll
-                    for (int cc = 0; cc < P::KCH; ++cc)
-                        kf[b][cc] = *reinterpret_cast<const uint4 *>(
-                            kbase + 2 * p * PG + 4 * b * D + 8 * ((ln.lg() * P::KCH + cc) ^ kz));
-                mp[p] = pair_scores<D>(kf, run_keep(p, t0, t1, vp, ln), pair_full(p, t0, t1),
-                                       qfrag, scale_log2, sv[p]);
-                M = fmaxf(M, mp[p]);
+                        for (int cc = 0; cc < P::KCH; ++cc)
+                            kf[b][cc] = *reinterpret_cast<const uint4 *>(
+                                kbase + 2 * p * PG + 4 * b * D +
+                                8 * ((ln.lg() * P::KCH + cc) ^ kz));
+                    mp[p] = pair_scores<D, true>(kf, all ? 8 : run_keep(p, t0, t1, vp, ln),
+                                                 all || pair_full(p, t0, t1), qfrag, scale_log2,
+                                                 sv[p]);
+                    M = fmaxf(M, mp[p]);
+                }
             }
-        }
+        };
+        if (whole)
+            pass1(std::true_type{});
+        else if (act)
+            pass1(std::false_type{});
         wait_dma_and_barrier();  // V pages of s in; K buffer free
         if (s + 1 < s_end)
             dma(k_img, k_cache, k_off, s + 1);
@@ -950,37 +1004,44 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
 #pragma unroll
         for (int db = 0; db < P::DB; ++db)
             a[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        auto pass2 = [&](auto all_c) {
+            constexpr bool all = decltype(all_c)::value;
 #pragma unroll
-        for (int p = 0; p < WAVES; ++p) {
-            if (p < npair) {
-                uint4 vf[P::DB];
+            for (int p = 0; p < WAVES; ++p) {
+                if (all || p < npair) {
+                    uint4 vf[P::DB];
 #pragma unroll
-                for (int db = 0; db < P::DB; ++db)
-                    vf[db] = *reinterpret_cast<const uint4 *>(vbase + 2 * p * PG + 16 * db * PAGE);
-                if (!pair_full(p, t0, t1))
-                    mask_runs<D>(vf, run_keep(p, t0, t1, vp, ln), vf);
-                float m_run = -INFINITY, l_run = 0.f;
-                f32x4_t acc[P::DB];
-                pair_pv<D, true>(sv[p], mp[p], vf, m_run, l_run, acc);
-                float l_w = l_run;
-                l_w += __shfl_xor(l_w, 16, kWave);
-                l_w += __shfl_xor(l_w, 32, kWave);
-                const float cw = (m_run == -INFINITY) ? 0.f : exp2_hw(m_run - M);
-                l = fmaf(cw, l_w, l);
+                    for (int db = 0; db < P::DB; ++db)
+                        vf[db] = *reinterpret_cast<const uint4 *>(vbase + 2 * p * PG +
+                                                                  16 * db * PAGE);
+                    if (!all && !pair_full(p, t0, t1))
+                        mask_runs<D>(vf, run_keep(p, t0, t1, vp, ln), vf);
+                    float m_run = -INFINITY, l_run = 0.f;
+                    f32x4_t acc[P::DB];
+                    pair_pv<D, true>(sv[p], mp[p], vf, m_run, l_run, acc);
+                    const float l_w = rows_sum<true>(l_run);
+                    const float cw = (m_run == -INFINITY) ? 0.f : exp2_hw(m_run - M);
+                    l = fmaf(cw, l_w, l);
+#pragma unroll
+                    for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            a[db][j] = fmaf(cw, acc[db][j], a[db][j]);
+                }
+            }
+        };
+        if (whole) {
+            pass2(std::true_type{});
+        } else {
+            pass2(std::false_type{});
+            if (npair < WAVES) {  // the decode's idle waves, each adding fma(0, +0, .)
+                l = fmaf(0.f, 0.f, l);
 #pragma unroll
                 for (int db = 0; db < P::DB; ++db)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        a[db][j] = fmaf(cw, acc[db][j], a[db][j]);
+                        a[db][j] = fmaf(0.f, 0.f, a[db][j]);
             }
-        }
-        if (npair < WAVES) {  // the decode's idle waves, each adding fma(0, +0, .)
-            l = fmaf(0.f, 0.f, l);
-#pragma unroll
-            for (int db = 0; db < P::DB; ++db)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    a[db][j] = fmaf(0.f, 0.f, a[db][j]);
         }
         // the split into the token's group, as the decode group kernel folds it
         {
