@@ -222,10 +222,8 @@ __device__ __forceinline__ void mask_runs(const uint4 (&src)[AttnK<D>::DB], int 
                              src[db].w & vmask[3]);
 }
 
-// The maximum and the sum of x over the four 16-lane rows of a wave, in the
-// butterfly order (lane i with i ^ 16, then with i ^ 32); every lane ends with
-// the same value, since at each step both lanes of a pair combine the same two
-// operands (fp32 max and addition commute).  LANES: the partner values come from
+// The maximum of x over the four 16-lane rows of a wave, in the butterfly order
+// (lane i with i ^ 16, then with i ^ 32); every lane ends with the same value.  LANES: the partner values come from
 // v_permlane16_swap / v_permlane32_swap, which exchange the odd 16-lane rows of
 // one operand with the even rows of the other (the upper 32 lanes of one with
 // the lower 32 of the other), so with x in both operands a lane gets its own
@@ -247,22 +245,6 @@ __device__ __forceinline__ float rows_max(float x)
     }
 }
 
-template <bool LANES>
-__device__ __forceinline__ float rows_sum(float x)
-{
-    if constexpr (LANES) {
-        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
-                                                        false, false);
-        x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-        const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                        false, false);
-        return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-    } else {
-        x += __shfl_xor(x, 16, kWave);
-        return x + __shfl_xor(x, 32, kWave);
-    }
-}
-
 // One page pair folded into the wave's running (m, l, acc) for the 16 query rows
 // whose fragments qfrag(cc) gives (head lr, d = lg * DPL + 8 * cc ..), with K from
 // k and V from v (already masked by mask_runs unless the pair is full).  Tokens
@@ -271,7 +253,8 @@ __device__ __forceinline__ float rows_sum(float x)
 //   m_new   = max(m_run, max_j s2_j)           (per head, over the 32 tokens)
 //   e_j     = 2^(s2_j - m_new),  p_j = hi_j + lo_j with hi_j = bf16(e_j),
 //             lo_j = bf16(e_j - hi_j)
-//   l_run   = fma(l_run, 2^(m_run - m_new), sum of this lane's p_j in token order)
+//   l_run   = fma(l_run, 2^(m_run - m_new), HI . 1 + LO . 1)  (the pair's sum of p_j
+//             per head, on MFMA against an operand of ones; the same in every lane)
 //   acc     = acc * 2^(m_run - m_new) + HI . V + LO . V  (bf16 MFMA, fp32 accumulate)
 // In two parts: pair_scores (s2 and the pair's maximum) and pair_pv (the rest).
 // FRESH: the state is the initial (-inf, 0, 0), for which the rescaling is the
@@ -312,9 +295,10 @@ __device__ __forceinline__ void pair_pv(const float (&sv)[2][4], float mloc,
 
     // p enters the bf16 P.V product as two bf16 parts, p_hi = bf16(p) and
     // p_lo = bf16(p - p_hi) (two MFMAs into one accumulator), so the weights carry
-    // 16 significant bits instead of 8; l sums the same p_hi + p_lo (exact in fp32).
+    // 16 significant bits instead of 8; l sums the same two parts, by the same two
+    // MFMAs against a V of ones, so every lane gets its head's sum over the pair's
+    // 32 tokens without a lane exchange.
     uint32_t pw[2][2], pl[2][2];  // bf16 p_hi / p_lo, two per word, token order in the run
-    float psum = 0.f;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -322,18 +306,21 @@ __device__ __forceinline__ void pair_pv(const float (&sv)[2][4], float mloc,
             const float e0 = exp2_hw(sv[b][j] - m_use), e1 = exp2_hw(sv[b][j + 1] - m_use);
             const uint32_t w = cvt_pk_bf16(e0, e1);
             const float h0 = __uint_as_float(w << 16), h1 = __uint_as_float(w & 0xffff0000u);
-            const uint32_t wl = cvt_pk_bf16(e0 - h0, e1 - h1);
-            psum += h0 + __uint_as_float(wl << 16);
-            psum += h1 + __uint_as_float(wl & 0xffff0000u);
             pw[b][j / 2] = w;
-            pl[b][j / 2] = wl;
+            pl[b][j / 2] = cvt_pk_bf16(e0 - h0, e1 - h1);
         }
     }
+    const bf16x8_t pf = as_bf16x8(make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
+    const bf16x8_t pfl = as_bf16x8(make_uint4(pl[0][0], pl[0][1], pl[1][0], pl[1][1]));
+    constexpr uint32_t kOnes = 0x3f803f80u;  // two bf16 1.0
+    const bf16x8_t ones = as_bf16x8(make_uint4(kOnes, kOnes, kOnes, kOnes));
+    f32x4_t ls = mfma_16x16x32_bf16(ones, pf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+    ls = mfma_16x16x32_bf16(ones, pfl, ls);
     if constexpr (FRESH) {
-        l_run = psum;
+        l_run = ls[0];
     } else {
         const float alpha = exp2_hw(m_run - m_use);  // of head lr, which all of acc is
-        l_run = fmaf(l_run, alpha, psum);
+        l_run = fmaf(l_run, alpha, ls[0]);
 #pragma unroll
         for (int db = 0; db < P::DB; ++db)
 #pragma unroll
@@ -342,8 +329,6 @@ __device__ __forceinline__ void pair_pv(const float (&sv)[2][4], float mloc,
     }
     m_run = m_new;
 
-    const bf16x8_t pf = as_bf16x8(make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
-    const bf16x8_t pfl = as_bf16x8(make_uint4(pl[0][0], pl[0][1], pl[1][0], pl[1][1]));
     // V as operand A, P as operand B: acc[db][j] is d = 16 * db + 4 * lg + j of head lr.
     // A fresh state's accumulator is +0, given to the first MFMA as a constant.
 #pragma unroll
@@ -379,20 +364,16 @@ __device__ __forceinline__ bool pair_full(int pr, int t0, int t1)
 }
 
 // A wave's (m, l, acc) into the workgroup's combine buffers ((m, l) head-major,
-// [head][wave]); l is the wave's sum for head lr over the four lane groups in
-// butterfly order.
+// [head][wave]); l_run, the wave's sum for head lr, is the same in every lane.
 template <int D>
 __device__ __forceinline__ void stash_wave(float m_run, float l_run,
                                            const f32x4_t (&acc)[AttnK<D>::DB], int wave,
                                            const PairLanes &ln, float (*c_m)[WAVES],
                                            float (*c_l)[WAVES], float (*c_acc)[16][D + CPAD])
 {
-    float l_w = l_run;
-    l_w += __shfl_xor(l_w, 16, kWave);
-    l_w += __shfl_xor(l_w, 32, kWave);
     if (ln.lg() == 0) {
         c_m[ln.lr()][wave] = m_run;
-        c_l[ln.lr()][wave] = l_w;
+        c_l[ln.lr()][wave] = l_run;
     }
 #pragma unroll
     for (int db = 0; db < AttnK<D>::DB; ++db)
@@ -517,7 +498,7 @@ __global__ __launch_bounds__(512, 2) void attn_split_kernel(
     const int valid_pages = (t1 - t0 + PAGE - 1) / PAGE;
 
     float m_run = -INFINITY;  // running max of head lr (log2 domain)
-    float l_run = 0.f;        // this lane's share of the running sum for head lr
+    float l_run = 0.f;        // the running sum for head lr (the same in every lane)
     f32x4_t acc[P::DB];       // acc[db][j]: d = 16*db + 4*lg + j of head lr
 #pragma unroll
     for (int db = 0; db < P::DB; ++db)
@@ -1019,9 +1000,8 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
                     float m_run = -INFINITY, l_run = 0.f;
                     f32x4_t acc[P::DB];
                     pair_pv<D, true>(sv[p], mp[p], vf, m_run, l_run, acc);
-                    const float l_w = rows_sum<true>(l_run);
                     const float cw = (m_run == -INFINITY) ? 0.f : exp2_hw(m_run - M);
-                    l = fmaf(cw, l_w, l);
+                    l = fmaf(cw, l_run, l);
 #pragma unroll
                     for (int db = 0; db < P::DB; ++db)
 #pragma unroll
