@@ -284,6 +284,44 @@ __device__ __forceinline__ float pair_scores(const uint4 (&k)[2][AttnK<D>::KCH],
     return rows_max<LANES>(mloc);
 }
 
+// pair_scores for NP fully live pairs at once (keep = 8, full): the same MFMA chain
+// per (pair, score block) and the same scaling, with the pairs' chains interleaved
+// so that consecutive MFMAs are independent.
+template <int D, int NP, typename QFrag>
+__device__ __forceinline__ void full_pairs_scores(const uint4 (&k)[NP][2][AttnK<D>::KCH],
+                                                  const QFrag &qfrag, float scale_log2,
+                                                  float (&sv)[NP][2][4], float (&mloc)[NP])
+{
+    using P = AttnK<D>;
+    f32x4_t sc[NP][2];
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            sc[i][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < P::KCH; ++cc) {
+        const bf16x8_t qf = qfrag(cc);
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                sc[i][b] = mfma_16x16x32_bf16(as_bf16x8(k[i][b][cc]), qf, sc[i][b]);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sv[i][b][j] = sc[i][b][j] * scale_log2;
+                m = fmaxf(m, sv[i][b][j]);
+            }
+        mloc[i] = rows_max<true>(m);
+    }
+}
+
 template <int D, bool FRESH>
 __device__ __forceinline__ void pair_pv(const float (&sv)[2][4], float mloc,
                                         const uint4 (&v)[AttnK<D>::DB], float &m_run,
@@ -886,11 +924,18 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
         v_off = 8 * pos;
     }
     auto pages_of = [&](int s) { return (min(s * S + S, Lmax) - s * S + PAGE - 1) / PAGE; };
-    auto dma = [&](uint16_t *img, const uint16_t *__restrict__ cache, int off, int s) {
+    // The block-table entries of split s, one per lane (lane < split_pages): read
+    // with one vector load a phase ahead of the copies that use them, which take
+    // each page id from its lane by v_readlane (no scalar load to wait for per page).
+    auto entries = [&](int s) {
+        return btrow[min(s * split_pages + min(lane, split_pages - 1), last_entry)];
+    };
+    auto dma = [&](uint16_t *img, const uint16_t *__restrict__ cache, int off, int s,
+                   int ent) {
         const int n = pages_of(s) * QPP;
         for (int i = wave; i < n; i += WAVES) {
             const int slot = i / QPP;
-            const int64_t phys = btrow[min(s * split_pages + slot, last_entry)];
+            const int64_t phys = __builtin_amdgcn_readlane(ent, slot);
             const uint16_t *src = cache + (phys * hkv + g) * PG + off;
             uint16_t *dst = img + slot * PG + (wave % QPP) * 512;
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -902,7 +947,8 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
 #endif
         }
     };
-    dma(k_img, k_cache, k_off, s_first);
+    int ent_cur = entries(s_first);
+    dma(k_img, k_cache, k_off, s_first, ent_cur);
 
     // the block's query tiles: token t's rows r = query head g * G + r (zero past G)
     for (int i = threadIdx.x; i < WAVES * 16 * CPR; i += WAVES * 64) {
@@ -937,7 +983,9 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
     for (int s = s_first; s < s_end; ++s) {
         const int t0 = s * S;
         wait_dma_and_barrier();  // K pages of s in (and the query tiles); V buffer free
-        dma(v_img, v_cache, v_off, s);
+        dma(v_img, v_cache, v_off, s, ent_cur);
+        // the next split's entries, for its K copies after the second barrier
+        const int ent_next = s + 1 < s_end ? entries(s + 1) : 0;
         const bool act = live && t0 < Lt;  // wave-uniform
         const int t1 = min(t0 + S, Lt);
         const int vp = (t1 - t0 + PAGE - 1) / PAGE;  // the token's pages in the split
@@ -948,33 +996,50 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
         const bool whole = act && S == 2 * PAGE * WAVES && t0 + S <= Lt;
         float sv[WAVES][2][4], mp[WAVES];
         float M = -INFINITY;
-        auto pass1 = [&](auto all_c) {
-            constexpr bool all = decltype(all_c)::value;
+        auto load_k = [&](int p, uint4 (&kf)[2][P::KCH]) {
 #pragma unroll
-            for (int p = 0; p < WAVES; ++p) {
-                if (all || p < npair) {
-                    uint4 kf[2][P::KCH];
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int cc = 0; cc < P::KCH; ++cc)
+                    kf[b][cc] = *reinterpret_cast<const uint4 *>(
+                        kbase + 2 * p * PG + 4 * b * D + 8 * ((ln.lg() * P::KCH + cc) ^ kz));
+        };
+        if (whole) {
+            // two pairs at a time: four independent MFMA chains in flight
+#pragma unroll
+            for (int p = 0; p < WAVES; p += 2) {
+                uint4 kf[2][2][P::KCH];
+                load_k(p, kf[0]);
+                load_k(p + 1, kf[1]);
+                float sv2[2][2][4], m2[2];
+                full_pairs_scores<D, 2>(kf, qfrag, scale_log2, sv2, m2);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
 #pragma unroll
                     for (int b = 0; b < 2; ++b)
 #pragma unroll
-                        for (int cc = 0; cc < P::KCH; ++cc)
-                            kf[b][cc] = *reinterpret_cast<const uint4 *>(
-                                kbase + 2 * p * PG + 4 * b * D +
-                                8 * ((ln.lg() * P::KCH + cc) ^ kz));
-                    mp[p] = pair_scores<D, true>(kf, all ? 8 : run_keep(p, t0, t1, vp, ln),
-                                                 all || pair_full(p, t0, t1), qfrag, scale_log2,
-                                                 sv[p]);
+                        for (int j = 0; j < 4; ++j)
+                            sv[p + i][b][j] = sv2[i][b][j];
+                    mp[p + i] = m2[i];
+                    M = fmaxf(M, m2[i]);
+                }
+            }
+        } else if (act) {
+#pragma unroll
+            for (int p = 0; p < WAVES; ++p) {
+                if (p < npair) {
+                    uint4 kf[2][P::KCH];
+                    load_k(p, kf);
+                    mp[p] = pair_scores<D, true>(kf, run_keep(p, t0, t1, vp, ln),
+                                                 pair_full(p, t0, t1), qfrag, scale_log2, sv[p]);
                     M = fmaxf(M, mp[p]);
                 }
             }
-        };
-        if (whole)
-            pass1(std::true_type{});
-        else if (act)
-            pass1(std::false_type{});
+        }
         wait_dma_and_barrier();  // V pages of s in; K buffer free
         if (s + 1 < s_end)
-            dma(k_img, k_cache, k_off, s + 1);
+            dma(k_img, k_cache, k_off, s + 1, ent_next);
+        ent_cur = ent_next;
         if (!act)
             continue;
 
