@@ -71,6 +71,8 @@ CASES = [
     (128, 4, 4, 256, 0, 1),               # one token, group of one
     (128, 64, 8, 256, 3000, 513),         # fused, group of 8, long prefix
     (128, 64, 4, 32, 250, 2100),          # fused, many splits per token
+    (64, 32, 4, 256, 0, 1100),            # fused, head_dim 64 with whole 256-token splits
+    (128, 12, 3, 256, 17, 700),           # fused, 3 kv heads (not dividing 8), group of 4
 ]
 
 
