@@ -286,8 +286,8 @@ int decode_attn_tuned(const void *q, int64_t q_row_stride, const void *k_cache,
  * kv_len = L_t (same absolute split boundaries, same per-split partial, same
  * ascending merge), so the output of token t is bit-identical to the
  * decode_attn_bi row for it, whatever start_pos, tokens and the chunking are.
- * Only the schedule differs: a workgroup loads each K/V page pair once and
- * serves a block of prompt tokens from it.
+ * Only the schedule differs: a workgroup copies each split's K/V pages of one kv
+ * head into LDS once and serves a block of 8 prompt tokens from them.
  * The chunk's K and V must already be in the cache (kv_append first).
  *  q              [tokens, num_q_heads, head_dim] bf16, row stride q_row_stride
  *  k_cache, v_cache  as for decode_attn_bi
@@ -302,7 +302,8 @@ int decode_attn_tuned(const void *q, int64_t q_row_stride, const void *k_cache,
  * Supported: head_dim 64 or 128; page_size 16; split_size a positive multiple of
  * page_size, at most 256 (one page pair per wave); a group of 1..16 query heads
  * per kv head; start_pos + tokens <= 2^30, tokens < 2^22, tokens * num_q_heads
- * < 2^25 and ceil((start_pos + tokens) / (4 * split_size)) < 2^22; 16-byte
+ * < 2^25, ceil(tokens / 8) * num_kv_heads < 2^22 and ceil((start_pos + tokens) /
+ * (4 * split_size)) < 2^22; 16-byte
  * aligned q, out and caches, row strides multiples of 8.  tokens == 0 is a no-op.
  */
 size_t prefill_attn_workspace_size(int64_t tokens, int num_q_heads, int num_kv_heads,

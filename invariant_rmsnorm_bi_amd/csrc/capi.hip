@@ -343,12 +343,13 @@ int prefill_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, co
     if (q_row_stride < (int64_t)hq * d || out_row_stride < (int64_t)hq * d || q_row_stride % 8 ||
         out_row_stride % 8)
         return RBI_EINVAL;
-    // fused: 512 threads per block of up to 8 tokens; split schedule: 512 per group of
-    // four splits, and the merge's 64 per (token, head)
+    // fused: 512 threads per (block of up to 8 tokens, kv head) in one grid dimension;
+    // split schedule: 512 per group of four splits, and the merge's 64 per (token, head)
     const int64_t groups = (start_pos + tokens + 4 * (int64_t)split_size - 1) /
                            (4 * (int64_t)split_size);
     if (start_pos + tokens > ((int64_t)1 << 30) || hkv > kGridYZ || tokens * 512 >= kMaxThreadsX ||
-        groups * 512 >= kMaxThreadsX || tokens * hq * 64 >= kMaxThreadsX)
+        (tokens + 7) / 8 * hkv * 512 >= kMaxThreadsX || groups * 512 >= kMaxThreadsX ||
+        tokens * hq * 64 >= kMaxThreadsX)
         return RBI_EUNSUPPORTED;
     const size_t need =
         rbi::prefill_workspace_bytes(tokens, hq, hkv, d, start_pos, split_size);
