@@ -1144,32 +1144,94 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(
 }
 
 // One thread per 16-byte chunk of a (token, kv head) row.  K rows are stored
-// token-major ([token][d]), V head-dim-major ([d][token]): the K chunk is copied
-// whole, the V chunk's 8 values go to 8 rows of the page.
+// token-major ([token][d]): the K chunk is copied whole.  V rows are stored
+// head-dim-major ([d][token]): the V chunk's 8 values go to 8 rows of the page.
+// Any head_dim (a multiple of 8) and page size.  32-bit index arithmetic: the host
+// bounds tokens * hkv * (d / 8) below 2^31.
 __global__ __launch_bounds__(256) void kv_append_kernel(
     const uint16_t *__restrict__ k_new, int64_t ks, const uint16_t *__restrict__ v_new, int64_t vs,
-    const int32_t *__restrict__ slots, int64_t tokens, uint16_t *__restrict__ k_cache,
+    const int32_t *__restrict__ slots, int tokens, uint16_t *__restrict__ k_cache,
     uint16_t *__restrict__ v_cache, int64_t num_pages, int hkv, int d, int page)
 {
     const int cpr = d / 8;  // chunks per head row
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int idx = (int)blockIdx.x * 256 + (int)threadIdx.x;
     if (idx >= tokens * hkv * cpr)
         return;
-    const int64_t t = idx / (hkv * cpr);
-    const int h = (int)((idx / cpr) % hkv);
-    const int c = (int)(idx % cpr);
+    const int t = idx / (hkv * cpr);
+    const int h = (idx / cpr) % hkv;
+    const int c = idx % cpr;
     const int64_t slot = slots[t];
     if (slot < 0 || slot >= num_pages * page)
         return;
     const int64_t pg = slot / page, off = slot % page;
     *reinterpret_cast<uint4 *>(k_cache + ((pg * hkv + h) * page + off) * d + 8 * c) =
-        *reinterpret_cast<const uint4 *>(k_new + t * ks + (int64_t)h * d + 8 * c);
-    const uint4 v = *reinterpret_cast<const uint4 *>(v_new + t * vs + (int64_t)h * d + 8 * c);
+        *reinterpret_cast<const uint4 *>(k_new + (int64_t)t * ks + h * d + 8 * c);
+    const uint4 v = *reinterpret_cast<const uint4 *>(v_new + (int64_t)t * vs + h * d + 8 * c);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint16_t *vd = v_cache + ((pg * hkv + h) * d + 8 * c) * page + off;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
         vd[(int64_t)e * page] = (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+}
+
+// Page size 16 and head_dim up to 128: one workgroup of 16 * (d / 8) threads per
+// (16 consecutive tokens, kv head), thread (t, c) holding chunk c of token t's row
+// as in kv_append_kernel.  When the 16 tokens fill one page in order (a prompt
+// chunk: slots page * 16 + 0 .. 15), their V chunks are transposed through LDS and
+// each head-dim row of the page is written whole (32 bytes, two 16-byte stores)
+// instead of as 16 separate 2-byte stores; otherwise (decode appends, ragged
+// chunks) every thread stores its chunk's 8 values as kv_append_kernel does.
+__global__ __launch_bounds__(256) void kv_append_page_kernel(
+    const uint16_t *__restrict__ k_new, int64_t ks, const uint16_t *__restrict__ v_new, int64_t vs,
+    const int32_t *__restrict__ slots, int tokens, uint16_t *__restrict__ k_cache,
+    uint16_t *__restrict__ v_cache, int64_t num_pages, int hkv, int d)
+{
+    constexpr int T = 16;  // tokens per workgroup = page size
+    __shared__ __attribute__((aligned(16))) uint16_t vt[T][128 + 8];
+    __shared__ int broken;
+    const int cpr = d / 8;
+    const int t0 = (int)blockIdx.x * T, h = (int)blockIdx.y;
+    const int t = (int)threadIdx.x / cpr, c = (int)threadIdx.x % cpr;
+    const bool real = t0 + t < tokens;
+    int64_t slot = real ? (int64_t)slots[t0 + t] : -1;
+    if (slot >= num_pages * T)
+        slot = -1;
+    if (threadIdx.x == 0)
+        broken = 0;
+    __syncthreads();
+    // the tile fills one page in order unless some token breaks the pattern
+    const int64_t first = real ? (int64_t)slots[t0] : -1;
+    if (c == 0 && (slot < 0 || first % T != 0 || slot != first + t || tokens - t0 < T))
+        broken = 1;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    const int64_t pg = slot / T, off = slot % T;
+    if (slot >= 0) {
+        *reinterpret_cast<uint4 *>(k_cache + ((pg * hkv + h) * T + off) * d + 8 * c) =
+            *reinterpret_cast<const uint4 *>(k_new + (int64_t)(t0 + t) * ks + h * d + 8 * c);
+        v = *reinterpret_cast<const uint4 *>(v_new + (int64_t)(t0 + t) * vs + h * d + 8 * c);
+    }
+    __syncthreads();  // broken settled
+    if (!broken) {
+        *reinterpret_cast<uint4 *>(&vt[t][8 * c]) = v;
+        __syncthreads();
+        uint16_t *vp = v_cache + (first / T * hkv + h) * (int64_t)d * T;
+        for (int i = threadIdx.x; i < 2 * d; i += T * cpr) {  // row dd, tokens 8 * half ..
+            const int dd = i >> 1, half = i & 1;
+            uint32_t w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                w[j] = (uint32_t)vt[8 * half + 2 * j][dd] |
+                       ((uint32_t)vt[8 * half + 2 * j + 1][dd] << 16);
+            *reinterpret_cast<uint4 *>(vp + (int64_t)dd * T + 8 * half) =
+                make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    } else if (slot >= 0) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint16_t *vd = v_cache + ((pg * hkv + h) * d + 8 * c) * T + off;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            vd[e * T] = (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+    }
 }
 
 template <int D>
@@ -1278,10 +1340,16 @@ hipError_t launch_kv_append(const uint16_t *k_new, int64_t ks, const uint16_t *v
                             uint16_t *v_cache, int64_t num_pages, int hkv, int d, int page,
                             hipStream_t s)
 {
+    if (page == 16 && d <= 128) {
+        const dim3 grid((unsigned)((tokens + 15) / 16), (unsigned)hkv), block(16 * (d / 8));
+        kv_append_page_kernel<<<grid, block, 0, s>>>(k_new, ks, v_new, vs, slots, (int)tokens,
+                                                     k_cache, v_cache, num_pages, hkv, d);
+        return hipGetLastError();
+    }
     const int64_t n = tokens * hkv * (d / 8);
     const dim3 grid((unsigned)((n + 255) / 256)), block(256);
-    kv_append_kernel<<<grid, block, 0, s>>>(k_new, ks, v_new, vs, slots, tokens, k_cache, v_cache,
-                                            num_pages, hkv, d, page);
+    kv_append_kernel<<<grid, block, 0, s>>>(k_new, ks, v_new, vs, slots, (int)tokens, k_cache,
+                                            v_cache, num_pages, hkv, d, page);
     return hipGetLastError();
 }
 

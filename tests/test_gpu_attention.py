@@ -272,6 +272,37 @@ def test_kv_append_exact_placement():
     assert float(vflat[~written].abs().max()) == 0
 
 
+@pytest.mark.parametrize("d,page", [(128, 16), (64, 16), (96, 16), (128, 8)])
+def test_kv_append_whole_pages_and_scattered(d, page):
+    # 48 tokens filling three pages in order (the whole-page path at page 16), five
+    # scattered, 17 from the middle of a page on, one out of range: every value at its
+    # slot, nothing else written
+    hkv, npages = 3, 24
+    kc = torch.zeros((npages, hkv, page, d), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros((npages, hkv, d, page), dtype=torch.bfloat16, device=DEV)
+    slot_list = [pg * page + i for pg in (3, 7, 1, 5, 9, 2) for i in range(page)][:48]
+    slot_list = slot_list + [n * page + page - 1 for n in (10, 11, 12, 13, 14)]
+    start = 20 * page + page // 2
+    slot_list += list(range(start, start + 17))
+    slot_list[50] = npages * page            # out of range: skipped
+    T = len(slot_list)
+    slots = torch.tensor(slot_list, dtype=torch.int32)
+    k_new = synth.normal((T, hkv * d), seed=61).to(DEV)
+    v_new = synth.normal((T, hkv * d), seed=62).to(DEV)
+    rbi.kv_append(k_new, v_new, slots.to(DEV), kc, vc)
+    kc_h, vc_h = kc.cpu(), vc.cpu()
+    kn, vn = k_new.cpu().view(T, hkv, d), v_new.cpu().view(T, hkv, d)
+    written = torch.zeros(npages * page, dtype=torch.bool)
+    for t in range(T):
+        s_ = int(slots[t])
+        if 0 <= s_ < npages * page:
+            assert torch.equal(kc_h[s_ // page, :, s_ % page], kn[t]), t
+            assert torch.equal(vc_h[s_ // page, :, :, s_ % page], vn[t]), t
+            written[s_] = True
+    assert float(kc_h.permute(0, 2, 1, 3).reshape(npages * page, -1)[~written].abs().max()) == 0
+    assert float(vc_h.permute(0, 3, 1, 2).reshape(npages * page, -1)[~written].abs().max()) == 0
+
+
 def test_tuned_twin_sensitivity():
     # the balanced twin picks a different split size for a lone long request than
     # for a full batch, so the probe's bits move
