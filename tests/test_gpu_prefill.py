@@ -98,6 +98,25 @@ def test_prefill_equals_decode_rows(d, hq, hkv, split, start, tokens):
     assert ok, (ratio, rows[worst])
 
 
+def test_prefill_bench_size_parity():
+    # the bench's prefill launch: one 4096-token prompt from position 0, 64 query / 4 kv
+    # heads of 128, split 256 (fused schedule, 2048 workgroups); every token bitwise
+    # equal to its decode row, the oracle on sampled tokens (split edges included)
+    T, HKV, HQ, D, S = 4096, 4, 64, 128, 256
+    print("prefill bench size", flush=True)
+    p = Prompt(T, HKV, HQ, D, seed=33)
+    p.append(0, T)
+    out = p.prefill(0, T, S)
+    ref_rows = p.decode_rows(0, T, S)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any()
+    diff = (out != ref_rows).reshape(T, -1).any(1).nonzero().flatten().tolist()
+    assert not diff, f"tokens differing from their decode rows: {diff[:10]}"
+    rows = [0, 1, 254, 255, 256, 1023, 1024, 2047, 2600, 4094, 4095]
+    ok, ratio, worst = attn_tol(out[rows], p.oracle_rows(rows), name="prefill 4096 tokens")
+    assert ok, (ratio, rows[worst])
+
+
 def test_prefill_schedules_as_documented():
     # the fused schedule (no workspace) once token blocks fill the GPU
     assert rbi.prefill_attn_workspace_size(700, 64, 4, 128, 0, 256) == 0
