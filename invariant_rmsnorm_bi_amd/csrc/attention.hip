@@ -8,11 +8,13 @@
 // splits grows with L.  The per-token reduction order is therefore a function
 // of the request's own length.
 //
-// Kernel 1 (one workgroup of 8 waves per (row, kv head, group of GROUP = 4
-// consecutive splits) for split sizes up to 256 tokens):
+// Kernel 1 (a workgroup of 8 waves per run of consecutive splits of one (row,
+// kv head), for split sizes up to 256 tokens: a group of GROUP = 4 splits, or,
+// for large batches, a whole row or a chunk of whole groups of it, taken longest
+// first from a plan that a one-workgroup kernel builds from the lengths):
 //   * each split's 16-token pages are dealt to the waves in pairs (wave w takes
 //     pages 2w and 2w+1), each pair loaded in one burst; the next split's pair is
-//     requested before the current one is processed (two register buffers);
+//     requested as soon as the current one's update is done;
 //   * scores S^T[token][head] = K . q^T with v_mfma_f32_16x16x32_bf16 (K rows are
 //     operand A, the group's query heads operand B; head_dim is the k dimension,
 //     lane group q = lane/16 carrying d = q*D/4 + 8c .. +7 in step c);
@@ -28,17 +30,21 @@
 //   * the eight waves' (m, l, acc) are combined in wave order 0 .. 7
 //     (M = max m, l = sum 2^(m_w - M) l_w, acc = sum 2^(m_w - M) acc_w) into the
 //     split's partial, and the group's splits are folded in ascending order (the
-//     fold below); the group's partial goes to the fp32 workspace.
+//     fold below); the group's partial goes to the fp32 workspace -- unless the
+//     workgroup holds the whole row, which folds its groups in ascending order
+//     itself, exactly as kernel 2 would, and writes the output.
 //   Longer splits (up to 1024 tokens): one workgroup per (row, kv head, split),
 //   each wave walking several pairs; a group is then one split.
 // Kernel 2 (one wave per (row, query head)): the same ascending fold over the
-//   row's group partials, then out = bf16(acc / l).  It always runs, even for a
-//   single group.  The whole reduction tree -- pairs, waves, splits, groups -- is
-//   a function of L alone.
-// No atomics: the final combine is a separate ordered clean-up pass.
+//   row's group partials, then out = bf16(acc / l), for every row not written
+//   whole by kernel 1 (even one with a single group).  The whole reduction tree
+//   -- pairs, waves, splits, groups -- is a function of L alone; which workgroup
+//   computes which part of it is the only thing the batch decides.
+// No atomics in any reduction (the plan's LDS atomics only order the work).
 //
 // The twin (decode_attn_tuned) runs the same kernels with a split size picked
 // from the batch shape, which moves the split boundaries with the batch.
+#include <atomic>
 #include <type_traits>
 
 #include "device.h"
@@ -587,60 +593,180 @@ __global__ __launch_bounds__(512, 2) void attn_split_kernel(
     }
 }
 
-// Splits of at most 2 * PAGE * WAVES tokens (one page pair per wave): one
-// workgroup per (row, kv head, group of GROUP consecutive splits).  Each split's
-// partial is formed exactly as a split workgroup would (wave w's pair 2w, 2w + 1
-// with a fresh state, the wave combine in order) and folded into the group's
-// running (M, l, acc) held by the combining threads; the group's partial goes to
-// the workspace.  A wave requests its pair of split s + 1 as soon as its update of
-// split s is done, so the loads run under the stash, the combine and the fold
-// (requesting it before the update, into a second register buffer, measured
-// slower: 1.85 vs 1.80 ms at the bench shape).  The stash is double-buffered
-// (split s uses buffer s % 2), so one barrier per split suffices.  One workgroup
-// per compute unit.
-template <int D>
+// Work plan of a decode call with a large batch (plan mode of attn_group_kernel),
+// built on the device from the lengths by attn_plan_kernel, int32 words:
+//   [0] items, [1] T (splits per chunk, a multiple of GROUP), [2..3] unused,
+//   then chunks[rows] (chunks of each row) and item_row, item_chunk[rows + kPlanCuMax].
+// Row r with n splits is cut into ceil(n / T) chunks of T consecutive splits (the
+// last one shorter); the items, one per (row, chunk), are ordered by size,
+// longest first.  T is the batch's work per compute unit, W / CUs with
+// W = hkv * sum of the rows' split counts, rounded up to whole groups, so every
+// chunk is at most one unit's share and the total count of items is at most
+// rows + CUs / hkv.  Only the schedule depends on the batch: a chunk's splits get
+// exactly the arithmetic of the grid mode, whichever workgroup takes them.
+constexpr int kPlanHdr = 4;
+constexpr int kPlanCuMax = 1024;   // compute units a plan has room for
+constexpr int kPlanKeys = 1024;    // size classes of the longest-first order
+__host__ __device__ constexpr int64_t plan_words(int64_t rows)
+{
+    return kPlanHdr + rows + 2 * (rows + kPlanCuMax);
+}
+
+// One workgroup: the plan above.  The order among items of equal size (and among
+// items of kPlanKeys - 1 splits or more) is whatever the LDS atomics give; it
+// decides only which workgroup takes an item.
+__global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t *__restrict__ kv_lens,
+                                                         int rows, int hkv, int S, int max_kv_len,
+                                                         int ncu, int32_t *__restrict__ plan)
+{
+    __shared__ int hist[kPlanKeys];
+    __shared__ int wave_tot[16];
+    __shared__ unsigned long long wsum;
+    __shared__ int T_s;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int *chunks = plan + kPlanHdr;
+    int *item_row = chunks + rows, *item_chunk = item_row + rows + kPlanCuMax;
+    hist[tid] = 0;
+    if (tid == 0)
+        wsum = 0;
+    __syncthreads();
+    unsigned long long part = 0;
+    for (int r = tid; r < rows; r += 1024)
+        part += (unsigned)((clamp_len(kv_lens[r], max_kv_len) + S - 1) / S);
+    atomicAdd(&wsum, part);
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned long long W = wsum * (unsigned long long)hkv;
+        unsigned long long t = (W + ncu - 1) / ncu;
+        t = (t + GROUP - 1) / GROUP * GROUP;
+        T_s = (int)(t < GROUP ? GROUP : (t > (1u << 30) ? (1u << 30) : t));
+        plan[1] = T_s;
+    }
+    __syncthreads();
+    const int T = T_s;
+    auto nsp_of = [&](int r) { return (clamp_len(kv_lens[r], max_kv_len) + S - 1) / S; };
+    for (int r = tid; r < rows; r += 1024) {
+        const int n = nsp_of(r), nc = (n + T - 1) / T;
+        chunks[r] = nc;
+        for (int c = 0; c < nc; ++c)
+            atomicAdd(&hist[min(min(T, n - c * T), kPlanKeys - 1)], 1);
+    }
+    __syncthreads();
+    // exclusive scan over the size classes, largest first: thread t holds class
+    // kPlanKeys - 1 - t
+    const int hv = hist[kPlanKeys - 1 - tid];
+    int inc = hv;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(inc, off, kWave);
+        if (lane >= off)
+            inc += u;
+    }
+    if (lane == 63)
+        wave_tot[wv] = inc;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wv; ++w)
+        base += wave_tot[w];
+    const int start = base + inc - hv;
+    __syncthreads();
+    hist[kPlanKeys - 1 - tid] = start;
+    if (tid == 1023)
+        plan[0] = base + inc;
+    __syncthreads();
+    for (int r = tid; r < rows; r += 1024) {
+        const int n = nsp_of(r), nc = (n + T - 1) / T;
+        for (int c = 0; c < nc; ++c) {
+            const int pos = atomicAdd(&hist[min(min(T, n - c * T), kPlanKeys - 1)], 1);
+            item_row[pos] = r;
+            item_chunk[pos] = c;
+        }
+    }
+}
+
+// Splits of at most 2 * PAGE * WAVES tokens (one page pair per wave).  A workgroup
+// takes a run of consecutive splits of one (row, kv head): in grid mode (plan
+// null) one group of GROUP splits, grid (groups * hkv, 1, rows); in plan mode the
+// plan's chunk blockIdx.x / hkv, grid (items bound * hkv).  Each split's partial is
+// formed exactly as a split workgroup would (wave w's pair 2w, 2w + 1 with a fresh
+// state, the wave combine in order) and folded into its group's running
+// (M, l, acc) held by the combining threads.  A finished group goes to the
+// workspace as the merge's partial -- or, when the chunk is the whole row, is
+// folded at once into the row's total as the merge would fold it, and the row's
+// output is written here (the merge then skips the row).  A wave requests its pair
+// of split s + 1 as soon as its update of split s is done, so the loads run under
+// the stash, the combine and the fold (requesting it before the update, into a
+// second register buffer, measured slower: 1.85 vs 1.80 ms at the bench shape).
+// The stash is double-buffered (split s uses buffer s % 2), so one barrier per
+// split suffices.  One workgroup per compute unit.
+//   Why whole rows: a workgroup cannot finish before its stores are written, and a
+// group partial store at the end of every workgroup, with the loads of the other
+// workgroups queued ahead of it, cost 14 % of the call at the bench shape (the
+// same kernel without them: 1511 vs 1749 us); a whole row stores 16 output rows
+// of bf16 once.  Longest chunks first keep the last compute units busy: in row
+// order the same kernel took 1654 us, longest first 1467.
+template <int D, bool PLAN>
 __global__ __launch_bounds__(512, 2) void attn_group_kernel(
     const uint16_t *__restrict__ q, int64_t q_row_stride, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_table,
     int64_t bt_stride, const int32_t *__restrict__ kv_lens, int hq, int hkv, int S,
-    int max_kv_len, int ngmax, float scale_log2, float *__restrict__ ws)
+    int max_kv_len, int ngmax, int rows, const int32_t *__restrict__ plan, float scale_log2,
+    float *__restrict__ ws, uint16_t *__restrict__ out, int64_t out_row_stride)
 {
     using P = AttnK<D>;
     __shared__ __attribute__((aligned(16))) uint16_t q_lds[16][QROW<D>];
     __shared__ __attribute__((aligned(16))) float c_m[2][16][WAVES], c_l[2][16][WAVES];
     __shared__ __attribute__((aligned(16))) float c_acc[2][WAVES][16][D + CPAD];
 
-    // grid x = group * hkv + kv head (the kv heads of a group back to back)
-    const int bx = xcd_rotated_x(hkv);
-    const int grp = bx / hkv, g = bx % hkv;
-    const int64_t r = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const PairLanes ln(lane);
     const int split_pages = S / PAGE;
     const int grp_pages = GROUP * split_pages;  // <= 64: one block-table entry per lane
     const int row_pages = (max_kv_len + PAGE - 1) / PAGE;
+    int64_t r;
+    int g, s_begin, run;  // run: splits in this workgroup's chunk (a bound in grid mode)
+    if constexpr (PLAN) {
+        const int item = (int)blockIdx.x / hkv;
+        g = (int)blockIdx.x % hkv;
+        if (item >= plan[0])
+            return;
+        run = plan[1];
+        r = plan[kPlanHdr + rows + item];
+        s_begin = plan[kPlanHdr + 2 * rows + kPlanCuMax + item] * run;
+    } else {
+        // grid x = group * hkv + kv head (the kv heads of a group back to back)
+        const int bx = xcd_rotated_x(hkv);
+        g = bx % hkv;
+        r = blockIdx.z;
+        s_begin = bx / hkv * GROUP;
+        run = GROUP;
+    }
     const int32_t *btrow = block_table + r * bt_stride;
-    // the group's block-table entries, read before the length (clamped into the
-    // table row; entries past the row's last page are never used)
-    const int my_page = btrow[min(grp * grp_pages + min(lane, grp_pages - 1), row_pages - 1)];
+    // group grp's block-table entries, one per lane (clamped into the table row;
+    // entries past the row's last page are never used)
+    auto entries = [&](int grp) {
+        return btrow[min(grp * grp_pages + min(lane, grp_pages - 1), row_pages - 1)];
+    };
+    int my_page = entries(s_begin / GROUP);  // read before the length
     const int L = clamp_len(kv_lens[r], max_kv_len);
     const int nsplit = (L + S - 1) / S;
-    const int s0 = grp * GROUP;
-    if (s0 >= nsplit)
+    if (s_begin >= nsplit)
         return;
-    const int s1 = min(s0 + GROUP, nsplit);
+    const int s_end = min(s_begin + run, nsplit);
+    const bool whole = PLAN && s_begin == 0 && s_end == nsplit;
+    int next_page = PLAN && s_begin + GROUP < s_end ? entries(s_begin / GROUP + 1) : my_page;
     const int G = hq / hkv;
 
-    // pages of split s: entries (s - s0) * split_pages .. of the group's my_page
+    // pages of split s: entries (s % GROUP) * split_pages .. of its group's entries
     auto vpages = [&](int s) { return (min(s * S + S, L) - s * S + PAGE - 1) / PAGE; };
     PairFrag<D> f;
-    auto load = [&](int s) {
+    auto load = [&](int s, int pages) {
         if (wave < (vpages(s) + 1) / 2)
-            load_pair<D>(f, wave, __shfl(my_page, (lane + (s - s0) * split_pages) & 63, kWave),
+            load_pair<D>(f, wave, __shfl(pages, (lane + (s % GROUP) * split_pages) & 63, kWave),
                          vpages(s), k_cache, v_cache, hkv, g, ln);
     };
 
-    load(s0);
+    load(s_begin, my_page);
     for (int i = threadIdx.x; i < 16 * D / 8; i += WAVES * 64) {
         const int h = i / (D / 8), c = i % (D / 8);
         *reinterpret_cast<uint4 *>(&q_lds[h][8 * c]) =
@@ -653,12 +779,17 @@ __global__ __launch_bounds__(512, 2) void attn_group_kernel(
     constexpr int EPT = D / 32;
     const int h = threadIdx.x >> 5;  // combining thread: head h, elements dq .. dq + EPT - 1
     const int dq = (threadIdx.x & 31) * EPT;
-    float Mg = -INFINITY, lg = 0.f, og[EPT];  // the group's fold so far
+    float Mg = -INFINITY, lg = 0.f, og[EPT];  // the current group's fold
+    float Mt = -INFINITY, lt = 0.f, ot[EPT];  // whole row: the fold of its groups
+    // a finished group's partial when more groups follow in the chunk: stored one
+    // split later, after that split's loads are requested
+    float pM = 0.f, pl = 0.f, po[EPT];
+    int pgrp = -1;
 #pragma unroll
     for (int e = 0; e < EPT; ++e)
-        og[e] = 0.f;
-    for (int s = s0; s < s1; ++s) {
-        const int buf = (s - s0) & 1;
+        og[e] = ot[e] = po[e] = 0.f;
+    for (int s = s_begin; s < s_end; ++s) {
+        const int buf = (s - s_begin) & 1;
         const int t0 = s * S, t1 = min(t0 + S, L);
         const int vp = vpages(s);
         float m_run = -INFINITY, l_run = 0.f;
@@ -674,8 +805,15 @@ __global__ __launch_bounds__(512, 2) void attn_group_kernel(
             pair_update<D, true>(f, f.v, keep, full, &q_lds[0][0], scale_log2, ln, m_run, l_run,
                                  acc);
         }
-        if (s + 1 < s1)
-            load(s + 1);
+        const bool grp_end = s % GROUP == GROUP - 1 || s + 1 == s_end;
+        if (s + 1 < s_end)
+            load(s + 1, PLAN && grp_end ? next_page : my_page);
+        if (PLAN && pgrp >= 0) {
+            if (h < G)
+                store_partial<D, EPT>(ws + part_off(r, g, pgrp, h, hkv, ngmax, G, IST<D>), dq, po,
+                                      pM, pl);
+            pgrp = -1;
+        }
         stash_wave<D>(m_run, l_run, acc, wave, ln, c_m[buf], c_l[buf], c_acc[buf]);
         // the split's stash complete; every combine of split s - 1 (which read the
         // other buffer) done before split s + 1 writes it
@@ -693,9 +831,48 @@ __global__ __launch_bounds__(512, 2) void attn_group_kernel(
                 og[e] = fold_step(og[e], al, be, os[e]);
             Mg = Mn;
         }
+        if (grp_end) {
+            if (PLAN && whole) {
+                if (h < G) {  // the group into the row's total, as the merge folds it
+                    const float Mn = fmaxf(Mt, Mg);
+                    const float al = exp2_hw(Mt - Mn), be = exp2_hw(Mg - Mn);
+                    lt = fold_step(lt, al, be, lg);
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e)
+                        ot[e] = fold_step(ot[e], al, be, og[e]);
+                    Mt = Mn;
+                }
+            } else if (s + 1 == s_end) {
+                if (h < G)
+                    store_partial<D, EPT>(ws + part_off(r, g, s / GROUP, h, hkv, ngmax, G, IST<D>),
+                                          dq, og, Mg, lg);
+            } else if constexpr (PLAN) {
+                pgrp = s / GROUP;
+                pM = Mg;
+                pl = lg;
+#pragma unroll
+                for (int e = 0; e < EPT; ++e)
+                    po[e] = og[e];
+            }
+            Mg = -INFINITY;
+            lg = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                og[e] = 0.f;
+            if (PLAN && s + 1 < s_end) {
+                my_page = next_page;
+                next_page = entries(s / GROUP + 2);
+            }
+        }
     }
-    if (h < G)
-        store_partial<D, EPT>(ws + part_off(r, g, grp, h, hkv, ngmax, G, IST<D>), dq, og, Mg, lg);
+    if (PLAN && whole && h < G) {
+        uint16_t *dst = out + r * out_row_stride + (int64_t)(g * G + h) * D + dq;
+        if constexpr (EPT == 4)
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(ot[0] / lt, ot[1] / lt),
+                                                         pack_bf16x2(ot[2] / lt, ot[3] / lt));
+        else
+            *reinterpret_cast<uint32_t *>(dst) = pack_bf16x2(ot[0] / lt, ot[1] / lt);
+    }
 }
 
 // One wave per (row, query head): the ascending fold of the row's partials, each
@@ -707,8 +884,8 @@ __global__ __launch_bounds__(512, 2) void attn_group_kernel(
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(
     const float *ws, const int32_t *__restrict__ kv_lens, int start, int64_t rows, int hq,
-    int hkv, int S, int max_kv_len, int nsmax, uint16_t *__restrict__ out,
-    int64_t out_row_stride)
+    int hkv, int S, int max_kv_len, int nsmax, const int32_t *__restrict__ row_chunks,
+    uint16_t *__restrict__ out, int64_t out_row_stride)
 {
     constexpr int EPL = D / 64;  // elements per lane
     constexpr int UNROLL = 16;
@@ -717,6 +894,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
     if (item >= rows * hq)
         return;
     const int64_t r = item / hq;
+    if (row_chunks && row_chunks[r] == 1)
+        return;  // a whole-row workgroup has written this row
     const int h = (int)(item % hq);
     const int L = kv_lens ? clamp_len(kv_lens[r], max_kv_len) : start + (int)r + 1;
     const int n = (L + S - 1) / S;  // splits of this row
@@ -1234,6 +1413,44 @@ __global__ __launch_bounds__(256) void kv_append_page_kernel(
     }
 }
 
+// Floats of group (or split) partials in the decode workspace; the plan, when the
+// split size has groups, follows them.
+int64_t partial_floats(int64_t rows, int hq, int d, int max_kv_len, int split)
+{
+    const int64_t nsmax = ((int64_t)max_kv_len + split - 1) / split;
+    const int64_t gs = splits_per_partial(split);
+    return rows * hq * ((nsmax + gs - 1) / gs) * (int64_t)(d + 4);
+}
+
+// Compute units of the current device, looked up once per device.
+int cu_count()
+{
+    constexpr int kDevMax = 64;
+    static std::atomic<int> cache[kDevMax];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevMax)
+        return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Plan mode (whole rows, longest first) when the batch gives the compute units at
+// least 1.5 (row, kv head) units each; below that a row's groups are spread over
+// many workgroups instead.  Measured at the bench's lengths (U{1..32768}, 64q/4kv,
+// d128, 256 CUs), plan against grid mode: batch 256 1469 vs 1745 us, 128 804 vs
+// 903, 96 661 vs 698, 64 494 vs 481, 32 231 vs 223.  Only the schedule changes,
+// never a bit of the output.
+bool use_plan(int64_t rows, int hkv, int ncu)
+{
+    return ncu > 0 && ncu <= kPlanCuMax && 2 * rows * hkv >= 3 * (int64_t)ncu &&
+           (rows + ncu / hkv + 1) * hkv < ((int64_t)1 << 22);  // the grid mode's x bound
+}
+
 template <int D>
 hipError_t launch_attn_d(const AttnArgs &a, hipStream_t s)
 {
@@ -1242,11 +1459,27 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t s)
     const int npmax = (nsmax + gs - 1) / gs;  // partials per (row, query head), at most
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const dim3 b1(WAVES * 64);
-    if (gs > 1)
-        attn_group_kernel<D><<<dim3((unsigned)(npmax * a.hkv), 1, (unsigned)a.rows), b1, 0, s>>>(
-            a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table, a.bt_stride, a.kv_lens,
-            a.hq, a.hkv, a.split, a.max_kv_len, npmax, scale_log2, a.ws);
-    else
+    const int32_t *row_chunks = nullptr;
+    if (gs > 1) {
+        const int ncu = cu_count();
+        if (use_plan(a.rows, a.hkv, ncu)) {
+            int32_t *plan = reinterpret_cast<int32_t *>(a.ws + partial_floats(a.rows, a.hq, a.d,
+                                                                              a.max_kv_len, a.split));
+            attn_plan_kernel<<<1, 1024, 0, s>>>(a.kv_lens, (int)a.rows, a.hkv, a.split,
+                                                a.max_kv_len, ncu, plan);
+            const int64_t items = a.rows + ncu / a.hkv + 1;
+            attn_group_kernel<D, true><<<dim3((unsigned)(items * a.hkv)), b1, 0, s>>>(
+                a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table, a.bt_stride, a.kv_lens,
+                a.hq, a.hkv, a.split, a.max_kv_len, npmax, (int)a.rows, plan, scale_log2, a.ws,
+                a.out, a.out_row_stride);
+            row_chunks = plan + kPlanHdr;
+        } else {
+            attn_group_kernel<D, false><<<dim3((unsigned)(npmax * a.hkv), 1, (unsigned)a.rows), b1, 0, s>>>(
+                a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table, a.bt_stride, a.kv_lens,
+                a.hq, a.hkv, a.split, a.max_kv_len, npmax, (int)a.rows, nullptr, scale_log2, a.ws,
+                a.out, a.out_row_stride);
+        }
+    } else
         attn_split_kernel<D><<<dim3((unsigned)(nsmax * a.hkv), 1, (unsigned)a.rows), b1, 0, s>>>(
             a.q, a.q_row_stride, a.k_cache, a.v_cache, a.block_table, a.bt_stride, a.kv_lens,
             a.hq, a.hkv, a.split, a.max_kv_len, nsmax, scale_log2, a.ws);
@@ -1256,7 +1489,7 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t s)
     const int64_t items = a.rows * a.hq;
     const dim3 g2((unsigned)((items + 3) / 4)), b2(256);
     attn_merge_kernel<D><<<g2, b2, 0, s>>>(a.ws, a.kv_lens, 0, a.rows, a.hq, a.hkv,
-                                           a.split * gs, a.max_kv_len, npmax, a.out,
+                                           a.split * gs, a.max_kv_len, npmax, row_chunks, a.out,
                                            a.out_row_stride);
     return hipGetLastError();
 }
@@ -1296,7 +1529,7 @@ hipError_t launch_prefill_sched(const PrefillArgs &a, hipStream_t s)
         const int64_t items = a.tokens * a.hq;
         attn_merge_kernel<D><<<dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s>>>(
             a.ws, nullptr, (int)a.start, a.tokens, a.hq, a.hkv, a.split * GROUP,
-            (int)(a.start + a.tokens), npmax, a.out, a.out_row_stride);
+            (int)(a.start + a.tokens), npmax, nullptr, a.out, a.out_row_stride);
         return hipGetLastError();
     }
 }
@@ -1312,9 +1545,8 @@ hipError_t launch_prefill_d(const PrefillArgs &a, hipStream_t s)
 
 size_t attn_workspace_bytes(int64_t rows, int hq, int d, int max_kv_len, int split)
 {
-    const int64_t nsmax = ((int64_t)max_kv_len + split - 1) / split;
-    const int64_t gs = splits_per_partial(split);
-    return (size_t)(rows * hq * ((nsmax + gs - 1) / gs)) * (size_t)(d + 4) * sizeof(float);
+    const int64_t plan = splits_per_partial(split) > 1 ? plan_words(rows) : 0;
+    return (size_t)(partial_floats(rows, hq, d, max_kv_len, split) + plan) * sizeof(float);
 }
 
 hipError_t launch_decode_attn(const AttnArgs &a, hipStream_t s)

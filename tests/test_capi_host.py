@@ -122,7 +122,9 @@ def test_decode_attn_validation():
     assert _attn(qs=64 * 128 - 8) == EINVAL
     assert _attn(ws=NULL) == EWORKSPACE
     need = rbi.decode_attn_workspace_size(4, 64, 128, 32768, 256)
-    assert need == 4 * 64 * 32 * 132 * 4      # 128 splits of 256 in 32 groups, 132-float slots
+    # 128 splits of 256 in 32 groups, 132-float slots; then the large-batch work plan:
+    # 4 header words, chunk counts per row, (row, chunk) per item for rows + 1024 items
+    assert need == 4 * 64 * 32 * 132 * 4 + plan_bytes(4)
     assert _attn(wsb=need - 1) == EWORKSPACE
     # bounds: lengths up to 2^30, rows <= 65535, (splits per row) * kv heads < 2^22
     # (512 threads each), rows * query heads < 2^25 (the merge's 64 threads each)
@@ -136,15 +138,23 @@ def test_decode_attn_validation():
     assert _attn(rows=32768, **wide) == EUNSUPPORTED
     assert _attn(rows=32767, wsb=1 << 20, **wide) == EWORKSPACE
     # the size query takes any int length without overflowing
-    assert rbi.decode_attn_workspace_size(1, 16, 64, (1 << 31) - 1, 16) == 16 * (1 << 25) * 68 * 4
+    assert (rbi.decode_attn_workspace_size(1, 16, 64, (1 << 31) - 1, 16)
+            == 16 * (1 << 25) * 68 * 4 + plan_bytes(1))
+
+
+def plan_bytes(rows):
+    """The large-batch work plan after the group partials: 4 header words, chunks per
+    row, and a (row, chunk) pair for each of up to rows + 1024 items."""
+    return (4 + rows + 2 * (rows + 1024)) * 4
 
 
 def test_decode_attn_workspace_depends_only_on_bounds():
     a = rbi.decode_attn_workspace_size(256, 64, 128, 32768, 256)
-    assert a == 256 * 64 * 32 * (128 + 4) * 4            # groups of 4 splits of 256
-    assert rbi.decode_attn_workspace_size(5, 4, 64, 63, 16) == 5 * 4 * 1 * 68 * 4
-    assert rbi.decode_attn_workspace_size(5, 4, 64, 65, 16) == 5 * 4 * 2 * 68 * 4
-    assert rbi.decode_attn_workspace_size(5, 4, 64, 4096, 512) == 5 * 4 * 8 * 68 * 4  # no groups
+    assert a == 256 * 64 * 32 * (128 + 4) * 4 + plan_bytes(256)  # groups of 4 splits of 256
+    assert rbi.decode_attn_workspace_size(5, 4, 64, 63, 16) == 5 * 4 * 1 * 68 * 4 + plan_bytes(5)
+    assert rbi.decode_attn_workspace_size(5, 4, 64, 65, 16) == 5 * 4 * 2 * 68 * 4 + plan_bytes(5)
+    # splits longer than 256 tokens: no groups, no plan
+    assert rbi.decode_attn_workspace_size(5, 4, 64, 4096, 512) == 5 * 4 * 8 * 68 * 4
 
 
 def test_tuned_split_size_follows_the_batch():

@@ -143,6 +143,41 @@ def test_c4_full_batch_sampled_parity_and_batch_invariance():
     assert int(bad) == 0, f"first seen by batch {first_bad}"
 
 
+def test_plan_mode_long_rows_in_chunks():
+    # A large batch (200 rows x 4 kv heads, at least two (row, kv head) units per
+    # compute unit) runs whole rows per workgroup, longest first.  Ten rows here are
+    # far longer than a compute unit's share of the batch, so they are cut into
+    # chunks of whole groups whose partials go through the merge, while the other
+    # rows are folded and written by one workgroup each.  Every row keeps the bits
+    # it has alone (grid mode), and the schedule, built with atomics, never changes
+    # the output from one call to the next.
+    rng = np.random.default_rng(31)
+    lens = [int(x) for x in rng.integers(1, 600, size=200)]
+    for i in range(0, 200, 20):
+        lens[i] = 32768 - 7 * i
+    kv = synth.paged_kv(lens, 4, 128, 16, max_pages=2048, device=DEV)
+    q = synth.normal((200, 64, 128), seed=32).to(DEV)
+    scale = 1 / math.sqrt(128)
+    out = _run(rbi.decode_attn_bi, q, kv, 32768)
+    rows = [0, 1, 20, 199]
+    ok, ratio, row = attn_tol(out[rows], _oracle(q, kv, scale, rows=rows), name="plan chunks")
+    assert ok, (ratio, row)
+    alone = torch.empty_like(out)
+    for r in range(200):
+        sub = synth.PagedKV(kv.k_cache, kv.v_cache, kv.block_table[r:r + 1].contiguous(),
+                            kv.kv_lens[r:r + 1].contiguous(), 16, 4, 128)
+        _run(rbi.decode_attn_bi, q[r:r + 1].contiguous(), sub, 32768, out=alone[r:r + 1])
+    assert torch.equal(alone, out)
+    again = torch.empty_like(out)
+    ws = torch.empty(rbi.decode_attn_workspace_size(200, 64, 128, 32768, 256),
+                     dtype=torch.uint8, device=DEV)
+    diff = torch.zeros((), dtype=torch.int64, device=DEV)
+    for _ in range(50):
+        _run(rbi.decode_attn_bi, q, kv, 32768, out=again, workspace=ws)
+        diff += (again != out).sum()
+    assert int(diff) == 0
+
+
 def test_grid_extent_and_page_placement_do_not_matter():
     lens = [300, 1000, 77]
     a = synth.paged_kv(lens, 4, 128, 16, seed=0, page_seed=3)
@@ -195,7 +230,9 @@ def test_kv_growth_across_split_boundaries():
         lens1 = torch.tensor([L], dtype=torch.int32, device=DEV)
         alone = rbi.decode_attn_bi(q, kc, vc, bt_pp_d, lens1, LMAX, S, workspace=ws1)
         # the row's partials: [kv head, group, query head of the kv group, acc | m | l | pad]
-        slots = ws1.view(torch.float32).view(HKV, npmax, HQ // HKV, D + 4)
+        # (the work plan of large batches follows them in the workspace)
+        slots = ws1.view(torch.float32)[: HKV * npmax * (HQ // HKV) * (D + 4)].view(
+            HKV, npmax, HQ // HKV, D + 4)
         for k in range(L // (S * GS)):
             if k in done:
                 assert torch.equal(slots[:, k], done[k]), (L, k)
