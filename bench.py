@@ -647,7 +647,8 @@ def main():
             k["graph_frac_hbm_peak"] = round(w["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4)
 
     dom = kernels["decode_attn_bi"]
-    roofline = {"bound": "hbm", "kernel": "decode_attn_bi (split + ordered merge)",
+    roofline = {"bound": "hbm",
+                "kernel": "decode_attn_bi (plan, whole-row split kernel, ordered merge)",
                 "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "algorithmic_bytes_per_launch": dom["bytes"], "avg_launch_us": dom["us"]}

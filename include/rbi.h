@@ -197,7 +197,7 @@ int matmul_tuned(const void *A, int64_t lda, const void *W, int64_t ldw, void *C
  *  max_kv_len   an upper bound on every kv_lens[r]; it sizes the grid and the
  *               workspace only -- results do not depend on it
  *  workspace    >= decode_attn_workspace_size(rows, num_q_heads, head_dim,
- *               max_kv_len, split_size) bytes, 16-byte aligned.  On return it holds
+ *               max_kv_len, split_size) bytes, 16-byte aligned.  It starts with
  *               the group partials: with GS = 4 splits per group when split_size
  *               <= 256 (else 1), np = ceil(ceil(max_kv_len / split_size) / GS),
  *               G = num_q_heads / num_kv_heads and query head h = g * G + hh, the
@@ -207,7 +207,17 @@ int matmul_tuned(const void *A, int64_t lda, const void *W, int64_t ldw, void *C
  *               weights 2^(score - m) as the P.V product takes them: each weight
  *               split into two bf16 parts, so 16 significant bits) and two zeros.
  *               One group's G slots are one contiguous block.  Groups past
- *               the row's last split are not written
+ *               the row's last split are not written.  When GS = 4, a work plan
+ *               of 4 + rows + 2 * (rows + 1024) int32 words follows the partials.
+ *               Large batches (rows * num_kv_heads at least 1.5 times the
+ *               device's compute units) use it: the call builds it on the device
+ *               from kv_lens, and each row whose split count is at most the
+ *               batch's work per compute unit is computed by one workgroup per
+ *               kv head, longest rows first, which folds the row's groups in the
+ *               same ascending order and writes out directly; that row's slots
+ *               are then not written.  Longer rows, and every row of a smaller
+ *               batch, go through the slots as above.  Either way every output
+ *               bit is the same
  * Supported: head_dim 64 or 128; page_size 16; split_size a positive multiple of
  * page_size, at most 1024; num_q_heads % num_kv_heads == 0 with a group of 1..16
  * query heads; max_kv_len <= 2^30; rows <= 65535, rows * num_q_heads < 2^25
@@ -233,12 +243,12 @@ int decode_attn_bi(const void *q, int64_t q_row_stride, const void *k_cache, con
  *  - Limit: decode_attn_workspace_size(rows, num_q_heads, head_dim, max_kv_len,
  *    split_size) <= RBI_NOALLOC_SCRATCH_BYTES (128 MiB), else RBI_EWORKSPACE with
  *    nothing enqueued (e.g. 64 query heads of 128 at split 256: rows *
- *    ceil(max_kv_len / 1024) <= 3971, so 124 rows at 32768 tokens).
+ *    ceil(max_kv_len / 1024) up to about 3970, so 124 rows at 32768 tokens).
  *  - The array is held by every device the library runs on until the process
  *    ends.  The first call on a device looks up its address there (no
  *    allocation); make that first call outside a graph capture.
  *  - Every call on one device shares that device's array, which keeps the last
- *    call's partials.  Calls that overlap on one device (two streams at once)
+ *    call's partials and plan.  Calls that overlap on one device (two streams at once)
  *    race and give undefined results; calls in one stream are ordered.
  *  - Nothing in the array needs to start at zero.  No hipMalloc, hipFree or
  *    other allocating routine is called.

@@ -291,8 +291,8 @@ int decode_attn_bi_noalloc(const void *q, int64_t q_row_stride, const void *k_ca
                               page_size, split_size, max_kv_len);
     if (st != RBI_OK || rows == 0)
         return st;
-    // every partial the merge reads is written by the same call first, so nothing in
-    // the scratch has to start at zero
+    // every partial the merge reads, and the work plan, are written by the same call
+    // first, so nothing in the scratch has to start at zero
     if (rbi::attn_workspace_bytes(rows, num_q_heads, head_dim, max_kv_len, split_size) >
         (size_t)RBI_NOALLOC_SCRATCH_BYTES)
         return RBI_EWORKSPACE;
