@@ -178,6 +178,33 @@ def test_plan_mode_long_rows_in_chunks():
     assert int(diff) == 0
 
 
+@pytest.mark.parametrize("d,hq,hkv,rows", [(64, 32, 4, 120), (128, 16, 2, 200), (128, 64, 8, 60),
+                                           (64, 8, 1, 400)])
+def test_plan_mode_shapes(d, hq, hkv, rows):
+    # large batches of other head shapes (rows * kv heads >= 384, so whole rows per
+    # workgroup on a 256-unit device): every row equals the same row alone, and
+    # sampled rows match the oracle
+    rng = np.random.default_rng(40 + d + hkv)
+    lens = [int(x) for x in rng.integers(1, 5000, size=rows)]
+    lens[3] = 1
+    lens[5] = 8192
+    kv = synth.paged_kv(lens, hkv, d, 16, max_pages=8192 // 16, device=DEV)
+    q = synth.normal((rows, hq, d), seed=41).to(DEV)
+    scale = 1 / math.sqrt(d)
+    out = _run(rbi.decode_attn_bi, q, kv, 8192, scale=scale)
+    sample = [0, 3, 5, rows - 1]
+    ok, ratio, row = attn_tol(out[sample], _oracle(q, kv, scale, rows=sample),
+                              name=f"plan d{d} {hq}/{hkv}")
+    assert ok, (ratio, row)
+    alone = torch.empty_like(out)
+    for r in range(rows):
+        sub = synth.PagedKV(kv.k_cache, kv.v_cache, kv.block_table[r:r + 1].contiguous(),
+                            kv.kv_lens[r:r + 1].contiguous(), 16, hkv, d)
+        _run(rbi.decode_attn_bi, q[r:r + 1].contiguous(), sub, 8192, out=alone[r:r + 1],
+             scale=scale)
+    assert torch.equal(alone, out)
+
+
 def test_grid_extent_and_page_placement_do_not_matter():
     lens = [300, 1000, 77]
     a = synth.paged_kv(lens, 4, 128, 16, seed=0, page_seed=3)
