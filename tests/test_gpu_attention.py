@@ -179,13 +179,13 @@ def test_plan_mode_long_rows_in_chunks():
 
 
 @pytest.mark.parametrize("d,hq,hkv,rows", [(64, 32, 4, 120), (128, 16, 2, 200), (128, 64, 8, 60),
-                                           (64, 8, 1, 400)])
+                                           (64, 8, 1, 400), (64, 8, 1, 1500)])
 def test_plan_mode_shapes(d, hq, hkv, rows):
     # large batches of other head shapes (rows * kv heads >= 384, so whole rows per
-    # workgroup on a 256-unit device): every row equals the same row alone, and
-    # sampled rows match the oracle
+    # workgroup on a 256-unit device; 1500 rows: more rows than the plan kernel has
+    # threads): every row equals the same row alone, and sampled rows match the oracle
     rng = np.random.default_rng(40 + d + hkv)
-    lens = [int(x) for x in rng.integers(1, 5000, size=rows)]
+    lens = [int(x) for x in rng.integers(1, 5000 if rows <= 400 else 2000, size=rows)]
     lens[3] = 1
     lens[5] = 8192
     kv = synth.paged_kv(lens, hkv, d, 16, max_pages=8192 // 16, device=DEV)
