@@ -603,11 +603,14 @@ __global__ __launch_bounds__(512, 2) void attn_split_kernel(
 //   then chunks[rows] (chunks of each row) and item_row, item_chunk[rows + kPlanCuMax].
 // Row r with n splits is cut into ceil(n / T) chunks of T consecutive splits (the
 // last one shorter); the items, one per (row, chunk), are ordered by size,
-// longest first.  T is the batch's work per compute unit, W / CUs with
-// W = hkv * sum of the rows' split counts, rounded up to whole groups, so every
-// chunk is at most one unit's share and the total count of items is at most
-// rows + CUs / hkv.  Only the schedule depends on the batch: a chunk's splits get
-// exactly the arithmetic of the grid mode, whichever workgroup takes them.
+// longest first.  T is 1.5 times the batch's work per compute unit, 1.5 W / CUs
+// with W = hkv * sum of the rows' split counts, rounded up to whole groups, so
+// the total count of items is at most rows + CUs / hkv.  (The call is bound by
+// HBM, so a unit that runs past its share while others finish gets more of the
+// bandwidth: whole rows up to 1.5 shares beat cutting them at one share, e.g.
+// batch 112 at the bench's lengths 709 vs 736 us; 1.25 and 2 shares measured as
+// 1.5.)  Only the schedule depends on the batch: a chunk's splits get exactly the
+// arithmetic of the grid mode, whichever workgroup takes them.
 constexpr int kPlanHdr = 4;
 constexpr int kPlanCuMax = 1024;   // compute units a plan has room for
 constexpr int kPlanKeys = 1024;    // size classes of the longest-first order
@@ -641,7 +644,7 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t *__restri
     __syncthreads();
     if (tid == 0) {
         const unsigned long long W = wsum * (unsigned long long)hkv;
-        unsigned long long t = (W + ncu - 1) / ncu;
+        unsigned long long t = (3 * W + 2ull * ncu - 1) / (2ull * ncu);
         t = (t + GROUP - 1) / GROUP * GROUP;
         T_s = (int)(t < GROUP ? GROUP : (t > (1u << 30) ? (1u << 30) : t));
         plan[1] = T_s;
@@ -1447,8 +1450,8 @@ int cu_count()
 // least 1.5 (row, kv head) units each; below that a row's groups are spread over
 // many workgroups instead.  Measured at the bench's lengths (U{1..32768}, 64q/4kv,
 // d128, 256 CUs), plan against grid mode: batch 256 1469 vs 1745 us, 128 804 vs
-// 903, 96 661 vs 698, 64 494 vs 481, 32 231 vs 223.  Only the schedule changes,
-// never a bit of the output.
+// 898, 112 709 vs 788, 96 652 vs 691, 64 494 vs 481, 32 231 vs 223.  Only the
+// schedule changes, never a bit of the output.
 bool use_plan(int64_t rows, int hkv, int ncu)
 {
     return ncu > 0 && ncu <= kPlanCuMax && 2 * rows * hkv >= 3 * (int64_t)ncu &&
