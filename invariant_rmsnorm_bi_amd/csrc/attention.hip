@@ -626,21 +626,33 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t *__restri
                                                          int rows, int hkv, int S, int max_kv_len,
                                                          int ncu, int32_t *__restrict__ plan)
 {
+    constexpr int kLdsRows = 4096;  // split counts kept in LDS for the first rows
     __shared__ int hist[kPlanKeys];
+    __shared__ int nsp_lds[kLdsRows];
     __shared__ int wave_tot[16];
     __shared__ unsigned long long wsum;
     __shared__ int T_s;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int *chunks = plan + kPlanHdr;
     int *item_row = chunks + rows, *item_chunk = item_row + rows + kPlanCuMax;
+    auto nsp_mem = [&](int r) { return (clamp_len(kv_lens[r], max_kv_len) + S - 1) / S; };
+    auto nsp_of = [&](int r) { return r < kLdsRows ? nsp_lds[r] : nsp_mem(r); };
     hist[tid] = 0;
     if (tid == 0)
         wsum = 0;
     __syncthreads();
     unsigned long long part = 0;
-    for (int r = tid; r < rows; r += 1024)
-        part += (unsigned)((clamp_len(kv_lens[r], max_kv_len) + S - 1) / S);
-    atomicAdd(&wsum, part);
+    for (int r = tid; r < rows; r += 1024) {
+        const int n = nsp_mem(r);
+        if (r < kLdsRows)
+            nsp_lds[r] = n;
+        part += (unsigned)n;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        part += __shfl_xor(part, off, kWave);
+    if (lane == 0)
+        atomicAdd(&wsum, part);
     __syncthreads();
     if (tid == 0) {
         const unsigned long long W = wsum * (unsigned long long)hkv;
@@ -651,7 +663,6 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t *__restri
     }
     __syncthreads();
     const int T = T_s;
-    auto nsp_of = [&](int r) { return (clamp_len(kv_lens[r], max_kv_len) + S - 1) / S; };
     for (int r = tid; r < rows; r += 1024) {
         const int n = nsp_of(r), nc = (n + T - 1) / T;
         chunks[r] = nc;
