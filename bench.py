@@ -250,7 +250,7 @@ def vendor_gemm_us(wl: Workload):
 
 
 def ceilings(wl: Workload):
-    """Read + write reference rates for RMSNorm on this machine: the library's plain
+    """Read + write reference rates for RMSNorm on this device: the library's plain
     streaming copy (rbi_stream_copy, one 16-byte chunk per thread) over the same
     four rotating 64 MiB input / output sets the RMSNorm leg uses, with ordinary and
     with non-temporal stores, graph-replayed like the per-kernel graph_us."""
