@@ -178,9 +178,11 @@ def test_plan_mode_long_rows_in_chunks():
     assert int(diff) == 0
 
 
-@pytest.mark.parametrize("d,hq,hkv,rows", [(64, 32, 4, 120), (128, 16, 2, 200), (128, 64, 8, 60),
-                                           (64, 8, 1, 400), (64, 8, 1, 1500)])
-def test_plan_mode_shapes(d, hq, hkv, rows):
+@pytest.mark.parametrize("d,hq,hkv,rows,split", [(64, 32, 4, 120, 256), (128, 16, 2, 200, 256),
+                                                 (128, 64, 8, 60, 256), (64, 8, 1, 400, 256),
+                                                 (64, 8, 1, 1500, 256), (128, 16, 2, 200, 64),
+                                                 (64, 4, 1, 400, 16)])
+def test_plan_mode_shapes(d, hq, hkv, rows, split):
     # large batches of other head shapes (rows * kv heads >= 384, so whole rows per
     # workgroup on a 256-unit device; 1500 rows: more rows than the plan kernel has
     # threads): every row equals the same row alone, and sampled rows match the oracle
@@ -191,17 +193,17 @@ def test_plan_mode_shapes(d, hq, hkv, rows):
     kv = synth.paged_kv(lens, hkv, d, 16, max_pages=8192 // 16, device=DEV)
     q = synth.normal((rows, hq, d), seed=41).to(DEV)
     scale = 1 / math.sqrt(d)
-    out = _run(rbi.decode_attn_bi, q, kv, 8192, scale=scale)
+    out = _run(rbi.decode_attn_bi, q, kv, 8192, split_size=split, scale=scale)
     sample = [0, 3, 5, rows - 1]
     ok, ratio, row = attn_tol(out[sample], _oracle(q, kv, scale, rows=sample),
-                              name=f"plan d{d} {hq}/{hkv}")
+                              name=f"plan d{d} {hq}/{hkv} split {split}")
     assert ok, (ratio, row)
     alone = torch.empty_like(out)
     for r in range(rows):
         sub = synth.PagedKV(kv.k_cache, kv.v_cache, kv.block_table[r:r + 1].contiguous(),
                             kv.kv_lens[r:r + 1].contiguous(), 16, hkv, d)
-        _run(rbi.decode_attn_bi, q[r:r + 1].contiguous(), sub, 8192, out=alone[r:r + 1],
-             scale=scale)
+        _run(rbi.decode_attn_bi, q[r:r + 1].contiguous(), sub, 8192, split_size=split,
+             out=alone[r:r + 1], scale=scale)
     assert torch.equal(alone, out)
 
 
