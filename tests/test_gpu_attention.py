@@ -207,6 +207,49 @@ def test_plan_mode_shapes(d, hq, hkv, rows, split):
     assert torch.equal(alone, out)
 
 
+def test_plan_mode_in_a_graph_follows_new_lengths():
+    # decode_attn_bi at batch 160 (the large-batch schedule) captured once as a HIP
+    # graph and replayed while the lengths change in place between replays, as a
+    # captured decode step's do: the plan is rebuilt on the device from the lengths
+    # at every replay, so each replay equals an eager call with those lengths
+    rows, lmax = 160, 8192
+    rng = np.random.default_rng(51)
+    lens0 = [int(x) for x in rng.integers(1, lmax - 600, size=rows)]
+    kv = synth.paged_kv([lmax] * rows, 4, 128, 16, max_pages=lmax // 16, device=DEV)
+    kv_lens = torch.tensor(lens0, dtype=torch.int32, device=DEV)
+    q = synth.normal((rows, 64, 128), seed=52).to(DEV)
+    out = torch.empty((rows, 64, 128), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(rbi.decode_attn_workspace_size(rows, 64, 128, lmax, 256),
+                     dtype=torch.uint8, device=DEV)
+
+    def call(o):
+        rbi.decode_attn_bi(q, kv.k_cache, kv.v_cache, kv.block_table, kv_lens, lmax, 256,
+                           out=o, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out)
+    eager = torch.empty_like(out)
+    for step in range(6):
+        # every row grows, a few by whole splits, and the longest rows change
+        grow = rng.integers(1, 120, size=rows) * (1 + (step % 3 == 2) * 4)
+        lens = [min(lmax, L + int(d)) for L, d in zip(kv_lens.tolist(), grow)]
+        lens[step * 7] = lmax
+        kv_lens.copy_(torch.tensor(lens, dtype=torch.int32))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        call(eager)
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), step
+
+
 def test_grid_extent_and_page_placement_do_not_matter():
     lens = [300, 1000, 77]
     a = synth.paged_kv(lens, 4, 128, 16, seed=0, page_seed=3)
